@@ -1,0 +1,152 @@
+/*
+ * beam_moe.h — C ABI of the Beam routed-MoE block on AMD Instinct MI355X (gfx950).
+ *
+ * The block (sources, cited by tag and section):
+ *   [S] "SGLang 原生支持 Reflection 的 Beam 并驱动其生产 API" (SGLang day-0 post for Beam)
+ *   [V] "vLLM 实现 Reflection Beam 501B MoE 模型 Day 0 支持" (vLLM day-0 post for Beam)
+ *   [H] "Reflection 发布 501B 开源模型 Beam，Apache 2.0 许可" (translated HF launch post)
+ *   1. FP32 router: logits = x . W_r^T with FP32 weights, accumulation and logits
+ *      ([V] §MoE and residual stream; [S] §Dense Layers and Grouped MoE Routing).
+ *   2. Sigmoid scores plus an expert correction bias choose the experts; group-limited selection:
+ *      G groups, group score = sum of its two largest biased scores, keep the best Gk groups, take
+ *      the top K experts over their union ([V] ibid.; [H] §专家混合).
+ *   3. Weights: the chosen experts' unbiased scores renormalised and multiplied by the routed
+ *      scale (2.5 for Beam), kept in FP32 ([V] ibid.; [S] ibid.).
+ *   4. K SwiGLU experts per token (hidden -> d_ff -> hidden, no biases) ([H] §专家混合), with the
+ *      bf16 rounding points of the BF16 expert kernels: gate/up outputs and the activation product
+ *      rounded to bf16, the FP32 routing weight applied to the down output before any rounding
+ *      ([S] §BF16 MoE Kernel Optimization).
+ *   5. Weighted combine over the K experts, no shared expert ([V] ibid.; [H] §专家混合).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and contiguous, with the
+ *     base address 16-byte aligned. Inputs are never written. Outputs and the workspace are fully
+ *     overwritten (plain stores, never accumulation).
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call is asynchronous on it; none
+ *     allocates device memory, frees, or synchronises the host.
+ *   - Every argument is validated on the host before the first launch: a non-zero status means
+ *     nothing was launched. T = 0 is a successful no-op. Device-side faults surface at the caller's
+ *     next synchronisation. Unsupported shapes or dtypes return BEAM_ERR_UNSUPPORTED: there is no
+ *     fallback path.
+ *   - Calls on distinct workspaces may run concurrently on different streams; calls that share a
+ *     workspace must be ordered by the caller.
+ *   - NaN or infinite inputs give undefined (but memory-safe) results.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define BEAM_API __attribute__((visibility("default")))
+#else
+#define BEAM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t beam_status_t;
+
+enum {
+  BEAM_OK = 0,
+  BEAM_ERR_NULL = 1,        /* a required pointer is NULL                                     */
+  BEAM_ERR_ALIGN = 2,       /* a pointer is not 16-byte aligned                               */
+  BEAM_ERR_SHAPE = 3,       /* T < 0, or dimensions inconsistent (e.g. E % G != 0, K > Gk*E/G) */
+  BEAM_ERR_DTYPE = 4,       /* unknown dtype code, or a combination the block does not define */
+  BEAM_ERR_UNSUPPORTED = 5, /* valid but not implemented for this shape (see the limits below) */
+  BEAM_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the *_workspace_bytes() figure  */
+  BEAM_ERR_ALIAS = 7,       /* an output overlaps an input or another output                  */
+  BEAM_ERR_LAUNCH = 8,      /* a kernel launch failed (the HIP error is reported by the runtime) */
+  BEAM_ERR_DEVICE = 9       /* no usable gfx950 device is current                             */
+};
+
+/* dtype codes */
+enum { BEAM_F32 = 0, BEAM_BF16 = 1, BEAM_FP8_E4M3 = 2 };
+
+/* Shape and numerics of one MoE layer.
+ *   hidden       H   model width (Beam 5120)
+ *   n_experts    E   routed experts (Beam 256)
+ *   n_groups     G   expert groups, contiguous, E/G experts each (Beam 8)
+ *   topk_groups  Gk  groups kept per token (Beam 4)
+ *   topk         K   experts per token (Beam 8)
+ *   d_ff         F   expert intermediate width (Beam 2560)
+ *   routed_scale     factor folded into the routing weights, so they sum to it (Beam 2.5)
+ *   x_dtype      BEAM_BF16 or BEAM_F32 (token activations)
+ *   w_dtype      BEAM_BF16, BEAM_FP8_E4M3 (with per-output-channel FP32 scales) or BEAM_F32 (expert
+ *                weights). BEAM_F32 experts require x_dtype BEAM_F32 and compute without any rounding
+ *                point; BEAM_BF16 / BEAM_FP8_E4M3 experts require x_dtype BEAM_BF16.
+ *   out_dtype    BEAM_F32 (graded output) or BEAM_BF16 (round-to-nearest-even copy)
+ * Limits of this build: H % 256 == 0, F % 256 == 0, E <= 256, E % 16 == 0 and (E <= 64 or
+ * E % 64 == 0), K <= 16, G <= 64, H * F < 2^31, T * K < 2^31. */
+typedef struct beam_moe_cfg {
+  int32_t hidden;
+  int32_t n_experts;
+  int32_t n_groups;
+  int32_t topk_groups;
+  int32_t topk;
+  int32_t d_ff;
+  float routed_scale;
+  int32_t x_dtype;
+  int32_t w_dtype;
+  int32_t out_dtype;
+} beam_moe_cfg;
+
+/* Routing only (steps 1–3).
+ *   x         [T][H] x_dtype
+ *   w_router  [E][H] fp32 — row e is expert e's router vector (the transpose of the H x E matrix)
+ *   bias      [E] fp32 correction bias (selection only; it never enters the weights)
+ *   topk_ids  [T][K] int32 out — chosen experts, biased score descending, ties to the lower id
+ *   topk_w    [T][K] fp32 out — routed_scale * s_k / sum_j s_j, s = sigmoid(logit) (unbiased)
+ *   workspace device scratch of at least beam_moe_route_workspace_bytes(cfg, T) bytes
+ * Ties between equal FP32 scores (groups or experts) go to the lower index. */
+BEAM_API beam_status_t beam_moe_route(const void* x, const float* w_router, const float* bias,
+                             int32_t* topk_ids, float* topk_w, int64_t T,
+                             const beam_moe_cfg* cfg, void* workspace, size_t workspace_bytes,
+                             void* stream);
+BEAM_API size_t beam_moe_route_workspace_bytes(const beam_moe_cfg* cfg, int64_t T);
+
+/* The whole block (steps 1–5).
+ *   x, w_router, bias      as for beam_moe_route
+ *   w_gate_up  [E][2F][H] w_dtype — rows [0, F) are the gate projection, rows [F, 2F) the up
+ *              projection; each row runs along H
+ *   w_down     [E][H][F]  w_dtype — each row runs along F
+ *   out        [T][H] out_dtype: out[t] = sum_k topk_w[t][k] * expert_{ids[t][k]}(x[t]), summed in
+ *              k order in FP32
+ *   w_gate_up_scale [E][2F], w_down_scale [E][H]: FP32 per-output-channel dequantisation scales
+ *              for BEAM_FP8_E4M3 weights; must be NULL otherwise. With FP8 weights the activations
+ *              are quantised on the fly: x per token and the intermediate h per row, each with
+ *              scale amax/448, codes rounded to nearest-even and saturated to +-448.
+ *   topk_ids_out [T][K] int32, topk_w_out [T][K] fp32: optional (NULL allowed) copies of the routing
+ *   workspace  device scratch of at least beam_moe_workspace_bytes(cfg, T) bytes */
+BEAM_API beam_status_t beam_moe_forward(const void* x, const float* w_router, const float* bias,
+                               const void* w_gate_up, const void* w_down, void* out, int64_t T,
+                               const beam_moe_cfg* cfg, const float* w_gate_up_scale,
+                               const float* w_down_scale, int32_t* topk_ids_out,
+                               float* topk_w_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+BEAM_API size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int64_t T);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+BEAM_API const char* beam_status_string(beam_status_t status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+BEAM_API int32_t beam_moe_version(void);
+
+/* Per-stage timing for measurement (not thread-safe; off by default).
+ * beam_moe_timing_enable(1) makes later forward/route calls record a HIP event pair around each
+ * stage on the call's stream; beam_moe_timing_collect() synchronises those events, writes per-stage
+ * totals (milliseconds) and launch counts for up to n_stages stages, releases the events and
+ * returns the number of stages defined. Stage order: 0 router logits, 1 router select,
+ * 2 moe_align, 3 activation quant (fp8), 4 gate/up GEMM, 5 h quant (fp8), 6 down GEMM,
+ * 7 combine. beam_moe_stage_name(i) names stage i. */
+BEAM_API void beam_moe_timing_enable(int32_t enable);
+BEAM_API int32_t beam_moe_timing_collect(double* total_ms, int32_t* launches, int32_t n_stages);
+BEAM_API const char* beam_moe_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BEAM_MOE_H */

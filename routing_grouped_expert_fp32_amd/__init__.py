@@ -1,0 +1,189 @@
+"""Python binding of libbeam_moe.so, the Beam routed-MoE block on MI355X (gfx950).
+
+Argument marshalling only: every step of the block runs in the library's HIP kernels. torch
+supplies device memory and the current stream. The functions mirror the C ABI in
+include/beam_moe.h (same names, same argument meaning). If the shared library is missing the
+import still works, but every call raises: there is no CPU fallback.
+
+Sources of the method (cited by tag and section in the library):
+  [S] "SGLang 原生支持 Reflection 的 Beam 并驱动其生产 API"
+  [V] "vLLM 实现 Reflection Beam 501B MoE 模型 Day 0 支持"
+  [H] "Reflection 发布 501B 开源模型 Beam，Apache 2.0 许可"
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "BEAM_F32", "BEAM_BF16", "BEAM_FP8_E4M3", "Cfg", "make_cfg", "lib", "lib_path", "route",
+    "forward", "workspace_bytes", "route_workspace_bytes", "BeamError", "timing_enable",
+    "timing_collect", "STAGES", "status_string",
+]
+
+BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
+_DT_CODE = {torch.float32: BEAM_F32, torch.bfloat16: BEAM_BF16, torch.uint8: BEAM_FP8_E4M3,
+            torch.float8_e4m3fn: BEAM_FP8_E4M3}
+STAGES = ["router_logits", "router_select", "moe_align", "quant_x_fp8", "gate_up", "quant_h_fp8",
+          "down", "combine"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libbeam_moe.so")
+
+
+class BeamError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float), ("x_dtype", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+def make_cfg(hidden=5120, n_experts=256, n_groups=8, topk_groups=4, topk=8, d_ff=2560,
+             routed_scale=2.5, x_dtype=BEAM_BF16, w_dtype=BEAM_BF16, out_dtype=BEAM_F32) -> Cfg:
+    return Cfg(hidden, n_experts, n_groups, topk_groups, topk, d_ff, routed_scale, x_dtype,
+               w_dtype, out_dtype)
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with "
+                               "`python -m routing_grouped_expert_fp32_amd.build` "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(lib_path)
+        vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
+        cfgp = ctypes.POINTER(Cfg)
+        L.beam_moe_route.argtypes = [vp, vp, vp, vp, vp, i64, cfgp, vp, sz, vp]
+        L.beam_moe_route.restype = i32
+        L.beam_moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, cfgp, vp, vp, vp, vp, vp, sz,
+                                       vp]
+        L.beam_moe_forward.restype = i32
+        L.beam_moe_workspace_bytes.argtypes = [cfgp, i64]
+        L.beam_moe_workspace_bytes.restype = sz
+        L.beam_moe_route_workspace_bytes.argtypes = [cfgp, i64]
+        L.beam_moe_route_workspace_bytes.restype = sz
+        L.beam_status_string.argtypes = [i32]
+        L.beam_status_string.restype = ctypes.c_char_p
+        L.beam_moe_version.argtypes = []
+        L.beam_moe_version.restype = i32
+        L.beam_moe_timing_enable.argtypes = [i32]
+        L.beam_moe_timing_enable.restype = None
+        L.beam_moe_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(i32), i32]
+        L.beam_moe_timing_collect.restype = i32
+        L.beam_moe_stage_name.argtypes = [i32]
+        L.beam_moe_stage_name.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().beam_status_string(status).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_bytes(cfg: Cfg, T: int) -> int:
+    return int(lib().beam_moe_workspace_bytes(ctypes.byref(cfg), T))
+
+
+def route_workspace_bytes(cfg: Cfg, T: int) -> int:
+    return int(lib().beam_moe_route_workspace_bytes(ctypes.byref(cfg), T))
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def route(x, w_router, bias, cfg: Cfg, topk_ids=None, topk_w=None, workspace=None, stream=None):
+    """beam_moe_route: returns (topk_ids int32 [T][K], topk_w fp32 [T][K])."""
+    T = x.shape[0]
+    if topk_ids is None:
+        topk_ids = torch.empty((T, cfg.topk), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, cfg.topk), dtype=torch.float32, device=x.device)
+    nbytes = route_workspace_bytes(cfg, T)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check_dev(x, w_router, bias, topk_ids, topk_w, workspace)
+    rc = lib().beam_moe_route(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_ids), _ptr(topk_w),
+                              T, ctypes.byref(cfg), _ptr(workspace), workspace.numel(),
+                              _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_route")
+    return topk_ids, topk_w
+
+
+def forward(x, w_router, bias, w_gate_up, w_down, cfg: Cfg, out=None, w_gate_up_scale=None,
+            w_down_scale=None, topk_ids_out=None, topk_w_out=None, workspace=None, stream=None):
+    """beam_moe_forward: returns out [T][H] (fp32 unless cfg.out_dtype is bf16)."""
+    T = x.shape[0]
+    if out is None:
+        odt = torch.bfloat16 if cfg.out_dtype == BEAM_BF16 else torch.float32
+        out = torch.empty((T, cfg.hidden), dtype=odt, device=x.device)
+    nbytes = workspace_bytes(cfg, T)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check_dev(x, w_router, bias, w_gate_up, w_down, out, w_gate_up_scale, w_down_scale,
+               topk_ids_out, topk_w_out, workspace)
+    rc = lib().beam_moe_forward(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up),
+                                _ptr(w_down), _ptr(out), T, ctypes.byref(cfg),
+                                _ptr(w_gate_up_scale), _ptr(w_down_scale), _ptr(topk_ids_out),
+                                _ptr(topk_w_out), _ptr(workspace), workspace.numel(),
+                                _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_forward")
+    return out
+
+
+def timing_enable(on: bool = True) -> None:
+    lib().beam_moe_timing_enable(1 if on else 0)
+
+
+def timing_collect() -> dict:
+    """{stage name: (total ms, launches)} of the calls made since timing was enabled."""
+    n = len(STAGES)
+    tot = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    lib().beam_moe_timing_collect(tot, cnt, n)
+    return {STAGES[i]: (tot[i], cnt[i]) for i in range(n)}
+
+
+@dataclass
+class WorkloadCfg:
+    """Helper: cfg of a synthgen workload shape."""
+
+    @staticmethod
+    def of(shape, x_dtype: str, w_dtype: str, out_dtype: str = "f32") -> Cfg:
+        code = {"f32": BEAM_F32, "bf16": BEAM_BF16, "fp8": BEAM_FP8_E4M3}
+        return make_cfg(shape.hidden, shape.n_experts, shape.n_groups, shape.topk_groups,
+                        shape.topk, shape.d_ff, shape.routed_scale, code[x_dtype], code[w_dtype],
+                        code[out_dtype])

@@ -1,0 +1,195 @@
+// moe_align: group the T*K routed slots by expert for the grouped GEMMs (gfx950).
+//
+// The TRTLLM MoE path the vLLM post lists ([V] "vLLM 实现 Reflection Beam 501B MoE 模型 Day 0 支持"
+// §The fused graph) has routing/permutation kernels between the router and the grouped GEMMs; this
+// is that step, designed for wave64:
+//   1. align_count   (one WG per chunk of 256 tokens): per expert, a 256-bit mask of which tokens
+//                    of the chunk chose it (LDS 64-bit atomic OR); popcounts give chunk counts.
+//   2. align_scan    (one WG of 1024 threads): per expert, exclusive prefix over chunks, expert
+//                    totals and offsets, and the row-block table: an expert with c rows gets
+//                    ceil(c/BM) blocks of near-equal size (sizes differ by at most one row), so a
+//                    block never carries more than BM-1 rows of padding and skewed experts split
+//                    into many equal blocks.
+//   3. align_scatter (one WG per chunk): each slot's row = expert offset + chunk base + number of
+//                    earlier tokens of the chunk that chose the same expert (popcount of the mask
+//                    below the token's bit). Rows of an expert are therefore in token order — a
+//                    deterministic, stable permutation; no sort, no global atomics.
+// Slots of one token name distinct experts (the router guarantees it).
+#include "common.h"
+
+namespace beam {
+
+constexpr int kChunk = kAlignChunk;
+constexpr int kWords = kAlignWords;
+
+__global__ __launch_bounds__(256) void align_count_kernel(const int32_t* __restrict__ ids,
+                                                          uint64_t* __restrict__ chunk_mask,
+                                                          int32_t* __restrict__ chunk_cnt,
+                                                          int64_t T, int E, int K) {
+  __shared__ unsigned long long mask[256 * kWords];
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < E * kWords; i += 256) mask[i] = 0ull;
+  __syncthreads();
+  const int64_t tbeg = (int64_t)c * kChunk;
+  const int ntok = (int)((T - tbeg) < kChunk ? (T - tbeg) : kChunk);
+  const int nslot = ntok * K;
+  for (int i = threadIdx.x; i < nslot; i += 256) {
+    const int tl = i / K;
+    const int e = ids[tbeg * K + i];
+    atomicOr(&mask[e * kWords + (tl >> 6)], 1ull << (tl & 63));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int cnt = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) {
+      const uint64_t m = mask[e * kWords + w];
+      chunk_mask[((int64_t)c * E + e) * kWords + w] = m;
+      cnt += __popcll(m);
+    }
+    chunk_cnt[(int64_t)c * E + e] = cnt;
+  }
+}
+
+// 1024 threads: 4 segments of the chunk range x 256 experts.
+__global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* __restrict__ chunk_base,
+                                                          int32_t* __restrict__ expert_count,
+                                                          int32_t* __restrict__ expert_off,
+                                                          int32_t* __restrict__ n_blocks,
+                                                          int32_t* __restrict__ blk_expert,
+                                                          int32_t* __restrict__ blk_row0,
+                                                          int32_t* __restrict__ blk_rows,
+                                                          int n_chunks, int E, int BM) {
+  __shared__ int seg_sum[4][256];
+  __shared__ int scan_rows[256];
+  __shared__ int scan_blks[256];
+  const int e = threadIdx.x & 255, seg = threadIdx.x >> 8;
+  const int per = (n_chunks + 3) / 4;
+  const int cb = seg * per, ce = min(n_chunks, cb + per);
+  // pass 1: segment totals (independent loads, unrolled so many are in flight)
+  int sum = 0;
+  if (e < E) {
+    int c = cb;
+    for (; c + 8 <= ce; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = chunk_base[(int64_t)(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; c < ce; ++c) sum += chunk_base[(int64_t)c * E + e];
+  }
+  seg_sum[seg][e] = sum;
+  __syncthreads();
+  // pass 2: exclusive prefix over chunks, in place (counts -> bases)
+  if (e < E) {
+    int run = 0;
+    for (int q = 0; q < seg; ++q) run += seg_sum[q][e];
+    int c = cb;
+    for (; c + 8 <= ce; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = chunk_base[(int64_t)(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        chunk_base[(int64_t)(c + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; c < ce; ++c) {
+      const int v = chunk_base[(int64_t)c * E + e];
+      chunk_base[(int64_t)c * E + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  // expert totals, offsets and block counts: exclusive scans over experts (threads 0..255)
+  int count = 0, nb = 0;
+  if (seg == 0) {
+    if (e < E) count = seg_sum[0][e] + seg_sum[1][e] + seg_sum[2][e] + seg_sum[3][e];
+    nb = (count + BM - 1) / BM;
+    scan_rows[e] = count;
+    scan_blks[e] = nb;
+  }
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int vr = 0, vb = 0;
+    if (seg == 0 && e >= off) {
+      vr = scan_rows[e - off];
+      vb = scan_blks[e - off];
+    }
+    __syncthreads();
+    if (seg == 0 && e >= off) {
+      scan_rows[e] += vr;
+      scan_blks[e] += vb;
+    }
+    __syncthreads();
+  }
+  if (seg == 0 && e < E) {
+    const int row_start = scan_rows[e] - count;   // inclusive -> exclusive
+    const int blk_start = scan_blks[e] - nb;
+    expert_count[e] = count;
+    expert_off[e] = row_start;
+    if (e == E - 1) {
+      expert_off[E] = scan_rows[e];
+      n_blocks[0] = scan_blks[e];
+    }
+    if (nb > 0) {
+      const int q = count / nb, rem = count % nb;
+      for (int i = 0; i < nb; ++i) {
+        blk_expert[blk_start + i] = e;
+        blk_row0[blk_start + i] = row_start + i * q + (i < rem ? i : rem);
+        blk_rows[blk_start + i] = q + (i < rem ? 1 : 0);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids,
+                                                            const uint64_t* __restrict__ chunk_mask,
+                                                            const int32_t* __restrict__ chunk_base,
+                                                            const int32_t* __restrict__ expert_off,
+                                                            int32_t* __restrict__ sorted_slot,
+                                                            int64_t T, int E, int K) {
+  __shared__ unsigned long long mask[256 * kWords];
+  __shared__ int base[256];
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < E * kWords; i += 256)
+    mask[i] = chunk_mask[(int64_t)c * E * kWords + i];
+  for (int e = threadIdx.x; e < E; e += 256)
+    base[e] = expert_off[e] + chunk_base[(int64_t)c * E + e];
+  __syncthreads();
+  const int64_t tbeg = (int64_t)c * kChunk;
+  const int ntok = (int)((T - tbeg) < kChunk ? (T - tbeg) : kChunk);
+  const int nslot = ntok * K;
+  for (int i = threadIdx.x; i < nslot; i += 256) {
+    const int tl = i / K;
+    const int e = ids[tbeg * K + i];
+    const int w = tl >> 6;
+    int rank = 0;
+    for (int q = 0; q < w; ++q) rank += __popcll(mask[e * kWords + q]);
+    const uint64_t below = (tl & 63) ? (mask[e * kWords + w] & ((1ull << (tl & 63)) - 1ull)) : 0ull;
+    rank += __popcll(below);
+    sorted_slot[base[e] + rank] = (int32_t)(tbeg * K + i);
+  }
+}
+
+hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
+                        hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  const int n_chunks = (int)ceil_div(s.T, kChunk);
+  hipLaunchKernelGGL(align_count_kernel, dim3(n_chunks), dim3(256), 0, st, ids, at.chunk_mask,
+                     at.chunk_base, s.T, s.E, s.K);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, st, at.chunk_base,
+                     at.expert_count, at.expert_off, at.n_blocks, at.blk_expert, at.blk_row0,
+                     at.blk_rows, n_chunks, s.E, BM);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(n_chunks), dim3(256), 0, st, ids, at.chunk_mask,
+                     at.chunk_base, at.expert_off, at.sorted_slot, s.T, s.E, s.K);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,369 @@
+// C ABI of the Beam MoE library: argument validation, workspace carving, kernel dispatch.
+// Declarations, argument meanings and error behaviour: include/beam_moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/beam_moe.h"
+#include "common.h"
+
+namespace {
+
+using beam::ceil_div;
+
+constexpr int kMaxDevices = 64;
+constexpr int kNumStages = 8;
+const char* kStageNames[kNumStages] = {"router_logits", "router_select", "moe_align",
+                                       "quant_x_fp8",   "gate_up",       "quant_h_fp8",
+                                       "down",          "combine"};
+
+size_t al256(size_t b) { return (b + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_bytes(int32_t dt) {
+  switch (dt) {
+    case BEAM_F32: return 4;
+    case BEAM_BF16: return 2;
+    case BEAM_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+// Block rows of moe_align for this call: small decode-like batches stream weights through 16-row
+// blocks; larger ones use the 128-row LDS-tiled kernels. FP32 experts use 16-row blocks.
+bool use_small_blocks(const beam_moe_cfg& c, int64_t T) {
+  return c.w_dtype == BEAM_F32 || T * c.topk <= 4 * (int64_t)c.n_experts;
+}
+int block_rows(const beam_moe_cfg& c, int64_t T) {
+  return use_small_blocks(c, T) ? beam::small_block_rows() : beam::tiled_block_rows();
+}
+
+struct Layout {
+  size_t sb = 0, ids = 0, w = 0, chunk_mask = 0, chunk_base = 0, expert_count = 0, expert_off = 0,
+         n_blocks = 0, blk_expert = 0, blk_row0 = 0, blk_rows = 0, sorted = 0, hbuf = 0, ybuf = 0,
+         xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
+  int64_t max_blocks = 0;
+  int bm = 0;
+};
+
+Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al256(bytes);
+    return o;
+  };
+  const int64_t E = c.n_experts, K = c.topk, TK = T * K;
+  L.sb = take(sizeof(float) * 2 * (size_t)(T * E));
+  if (full) {
+    const int64_t n_chunks = ceil_div(T, beam::kAlignChunk);
+    L.bm = block_rows(c, T);
+    L.max_blocks = beam::max_row_blocks(TK, E, L.bm);
+    L.ids = take(sizeof(int32_t) * (size_t)TK);
+    L.w = take(sizeof(float) * (size_t)TK);
+    L.chunk_mask = take(sizeof(uint64_t) * beam::kAlignWords * (size_t)(n_chunks * E));
+    L.chunk_base = take(sizeof(int32_t) * (size_t)(n_chunks * E));
+    L.expert_count = take(sizeof(int32_t) * (size_t)E);
+    L.expert_off = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.n_blocks = take(sizeof(int32_t));
+    L.blk_expert = take(sizeof(int32_t) * (size_t)L.max_blocks);
+    L.blk_row0 = take(sizeof(int32_t) * (size_t)L.max_blocks);
+    L.blk_rows = take(sizeof(int32_t) * (size_t)L.max_blocks);
+    L.sorted = take(sizeof(int32_t) * (size_t)TK);
+    const size_t hel = c.w_dtype == BEAM_F32 ? 4 : 2;
+    L.hbuf = take(hel * (size_t)TK * (size_t)c.d_ff);
+    L.ybuf = take(sizeof(float) * (size_t)TK * (size_t)c.hidden);
+    if (c.w_dtype == BEAM_FP8_E4M3) {
+      L.xq = take((size_t)T * (size_t)c.hidden);
+      L.xs = take(sizeof(float) * (size_t)T);
+      L.hq = take((size_t)TK * (size_t)c.d_ff);
+      L.hs = take(sizeof(float) * (size_t)TK);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+beam_status_t check_cfg(const beam_moe_cfg* c, bool experts) {
+  if (!c) return BEAM_ERR_NULL;
+  if (c->hidden <= 0 || c->n_experts <= 0 || c->n_groups <= 0 || c->topk_groups <= 0 ||
+      c->topk <= 0 || (experts && c->d_ff <= 0))
+    return BEAM_ERR_SHAPE;
+  if (c->n_experts % c->n_groups != 0 || c->topk_groups > c->n_groups ||
+      c->topk > c->topk_groups * (c->n_experts / c->n_groups))
+    return BEAM_ERR_SHAPE;
+  if (!(std::isfinite(c->routed_scale) && c->routed_scale > 0.f)) return BEAM_ERR_SHAPE;
+  const bool xd = c->x_dtype == BEAM_F32 || c->x_dtype == BEAM_BF16;
+  const bool wd = c->w_dtype == BEAM_F32 || c->w_dtype == BEAM_BF16 || c->w_dtype == BEAM_FP8_E4M3;
+  const bool od = c->out_dtype == BEAM_F32 || c->out_dtype == BEAM_BF16;
+  if (!xd || !wd || !od) return BEAM_ERR_DTYPE;
+  if ((c->x_dtype == BEAM_F32) != (c->w_dtype == BEAM_F32)) return BEAM_ERR_DTYPE;
+  // limits of this build
+  if (c->hidden % 256 != 0 || c->n_experts > 256 || c->n_experts % 16 != 0 ||
+      (c->n_experts > 64 && c->n_experts % 64 != 0) || c->n_groups > 64 || c->topk > 16)
+    return BEAM_ERR_UNSUPPORTED;
+  if (experts) {
+    if (c->d_ff % 256 != 0 || (int64_t)c->hidden * c->d_ff >= (int64_t(1) << 31))
+      return BEAM_ERR_UNSUPPORTED;
+    if (c->w_dtype == BEAM_FP8_E4M3) return BEAM_ERR_UNSUPPORTED;  // not in this build yet
+  }
+  return BEAM_OK;
+}
+
+beam_status_t check_T(const beam_moe_cfg* c, int64_t T) {
+  if (T < 0) return BEAM_ERR_SHAPE;
+  if (T * c->topk >= (int64_t(1) << 31) || T >= (int64_t(1) << 31)) return BEAM_ERR_UNSUPPORTED;
+  return BEAM_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range rng(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + bytes};
+}
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// every output must be disjoint from every input and every other output
+bool any_alias(const std::vector<Range>& ins, const std::vector<Range>& outs) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    for (const auto& r : ins)
+      if (r.lo != r.hi && overlap(outs[i], r)) return true;
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (outs[j].lo != outs[j].hi && overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+beam_status_t check_device() {
+  static int arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BEAM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BEAM_ERR_DEVICE;
+    arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return arch_ok[dev] == 1 ? BEAM_OK : BEAM_ERR_DEVICE;
+}
+
+// ---- stage timing ------------------------------------------------------------------------------
+struct TimingRec {
+  int stage;
+  hipEvent_t a, b;
+};
+std::vector<TimingRec> g_recs;
+bool g_timing = false;
+
+struct StageTimer {
+  int stage;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  StageTimer(int s, hipStream_t stream) : stage(s), st(stream) {
+    if (!g_timing) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      a = b = nullptr;
+      return;
+    }
+    hipEventRecord(a, st);
+  }
+  ~StageTimer() {
+    if (!a) return;
+    hipEventRecord(b, st);
+    g_recs.push_back({stage, a, b});
+  }
+};
+
+#define LAUNCH(stage, expr)                               \
+  do {                                                    \
+    StageTimer timer_((stage), st);                       \
+    if ((expr) != hipSuccess) return BEAM_ERR_LAUNCH;     \
+  } while (0)
+
+beam::Shape shape_of(const beam_moe_cfg& c, int64_t T) {
+  return beam::Shape{T, c.hidden, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.d_ff,
+                     c.routed_scale};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* beam_status_string(beam_status_t s) {
+  switch (s) {
+    case BEAM_OK: return "ok";
+    case BEAM_ERR_NULL: return "null pointer";
+    case BEAM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case BEAM_ERR_SHAPE: return "inconsistent shape";
+    case BEAM_ERR_DTYPE: return "unsupported dtype combination";
+    case BEAM_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case BEAM_ERR_WORKSPACE: return "workspace missing or too small";
+    case BEAM_ERR_ALIAS: return "output overlaps another buffer";
+    case BEAM_ERR_LAUNCH: return "kernel launch failed";
+    case BEAM_ERR_DEVICE: return "no gfx950 device current";
+    default: return "unknown status";
+  }
+}
+
+int32_t beam_moe_version(void) { return 100; }
+
+size_t beam_moe_route_workspace_bytes(const beam_moe_cfg* cfg, int64_t T) {
+  if (check_cfg(cfg, false) != BEAM_OK || T < 0) return 0;
+  return make_layout(*cfg, T, false).total;
+}
+
+size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int64_t T) {
+  if (check_cfg(cfg, true) != BEAM_OK || T < 0) return 0;
+  return make_layout(*cfg, T, true).total;
+}
+
+beam_status_t beam_moe_route(const void* x, const float* w_router, const float* bias,
+                             int32_t* topk_ids, float* topk_w, int64_t T,
+                             const beam_moe_cfg* cfg, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  beam_status_t rc = check_cfg(cfg, false);
+  if (rc != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if (T == 0) return BEAM_OK;
+  const beam_moe_cfg& c = *cfg;
+  if (!x || !w_router || !bias || !topk_ids || !topk_w || !workspace) return BEAM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(bias) || !aligned16(topk_ids) ||
+      !aligned16(topk_w) || !aligned16(workspace))
+    return BEAM_ERR_ALIGN;
+  const Layout L = make_layout(c, T, false);
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+  const size_t TK = (size_t)(T * c.topk);
+  const std::vector<Range> ins = {rng(x, (size_t)T * c.hidden * dtype_bytes(c.x_dtype)),
+                                  rng(w_router, sizeof(float) * c.n_experts * c.hidden),
+                                  rng(bias, sizeof(float) * c.n_experts)};
+  const std::vector<Range> outs = {rng(topk_ids, sizeof(int32_t) * TK),
+                                   rng(topk_w, sizeof(float) * TK), rng(workspace, L.total)};
+  if (any_alias(ins, outs)) return BEAM_ERR_ALIAS;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
+  const beam::Shape s = shape_of(c, T);
+  LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
+  LAUNCH(1, beam::launch_router_select(sb, topk_ids, topk_w, s, st));
+  return BEAM_OK;
+}
+
+beam_status_t beam_moe_forward(const void* x, const float* w_router, const float* bias,
+                               const void* w_gate_up, const void* w_down, void* out, int64_t T,
+                               const beam_moe_cfg* cfg, const float* w_gate_up_scale,
+                               const float* w_down_scale, int32_t* topk_ids_out,
+                               float* topk_w_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  beam_status_t rc = check_cfg(cfg, true);
+  if (rc != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  const beam_moe_cfg& c = *cfg;
+  const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
+  if (!fp8 && (w_gate_up_scale || w_down_scale)) return BEAM_ERR_DTYPE;
+  if (T == 0) return BEAM_OK;
+  if (!x || !w_router || !bias || !w_gate_up || !w_down || !out || !workspace) return BEAM_ERR_NULL;
+  if (fp8 && (!w_gate_up_scale || !w_down_scale)) return BEAM_ERR_NULL;
+  const void* ptrs[] = {x, w_router, bias, w_gate_up, w_down, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BEAM_ERR_ALIGN;
+  if ((topk_ids_out && !aligned16(topk_ids_out)) || (topk_w_out && !aligned16(topk_w_out)) ||
+      (w_gate_up_scale && !aligned16(w_gate_up_scale)) || (w_down_scale && !aligned16(w_down_scale)))
+    return BEAM_ERR_ALIGN;
+  const Layout L = make_layout(c, T, true);
+  if (L.max_blocks > 65535) return BEAM_ERR_UNSUPPORTED;   // grid.y bound of the GEMM launches
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+
+  const size_t H = c.hidden, E = c.n_experts, F = c.d_ff, TK = (size_t)(T * c.topk);
+  const size_t wb = dtype_bytes(c.w_dtype);
+  std::vector<Range> ins = {rng(x, (size_t)T * H * dtype_bytes(c.x_dtype)),
+                            rng(w_router, sizeof(float) * E * H), rng(bias, sizeof(float) * E),
+                            rng(w_gate_up, wb * E * 2 * F * H), rng(w_down, wb * E * H * F)};
+  if (fp8) {
+    ins.push_back(rng(w_gate_up_scale, sizeof(float) * E * 2 * F));
+    ins.push_back(rng(w_down_scale, sizeof(float) * E * H));
+  }
+  std::vector<Range> outs = {rng(out, (size_t)T * H * dtype_bytes(c.out_dtype)),
+                             rng(workspace, L.total)};
+  if (topk_ids_out) outs.push_back(rng(topk_ids_out, sizeof(int32_t) * TK));
+  if (topk_w_out) outs.push_back(rng(topk_w_out, sizeof(float) * TK));
+  if (any_alias(ins, outs)) return BEAM_ERR_ALIAS;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  beam::AlignTables at;
+  at.chunk_mask = reinterpret_cast<uint64_t*>(ws + L.chunk_mask);
+  at.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  at.expert_count = reinterpret_cast<int32_t*>(ws + L.expert_count);
+  at.expert_off = reinterpret_cast<int32_t*>(ws + L.expert_off);
+  at.n_blocks = reinterpret_cast<int32_t*>(ws + L.n_blocks);
+  at.blk_expert = reinterpret_cast<int32_t*>(ws + L.blk_expert);
+  at.blk_row0 = reinterpret_cast<int32_t*>(ws + L.blk_row0);
+  at.blk_rows = reinterpret_cast<int32_t*>(ws + L.blk_rows);
+  at.sorted_slot = reinterpret_cast<int32_t*>(ws + L.sorted);
+  float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
+  const beam::Shape s = shape_of(c, T);
+  const bool small = use_small_blocks(c, T);
+
+  LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
+  LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  LAUNCH(2, beam::launch_align(ids, at, s, L.bm, st));
+  if (c.w_dtype == BEAM_F32) {
+    float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
+    LAUNCH(4, beam::launch_gate_up_f32(reinterpret_cast<const float*>(x),
+                                       reinterpret_cast<const float*>(w_gate_up), hbuf, at, s,
+                                       L.max_blocks, st));
+    LAUNCH(6, beam::launch_down_f32(hbuf, reinterpret_cast<const float*>(w_down), tw, ybuf, at, s,
+                                    L.max_blocks, st));
+  } else {
+    uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
+    LAUNCH(4, beam::launch_gate_up_bf16(reinterpret_cast<const uint16_t*>(x),
+                                        reinterpret_cast<const uint16_t*>(w_gate_up), hbuf, at, s,
+                                        L.max_blocks, small, st));
+    LAUNCH(6, beam::launch_down_bf16(hbuf, reinterpret_cast<const uint16_t*>(w_down), tw, ybuf,
+                                     at, s, L.max_blocks, small, st));
+  }
+  LAUNCH(7, beam::launch_combine(ybuf, out, c.out_dtype == BEAM_BF16, s, st));
+  return BEAM_OK;
+}
+
+void beam_moe_timing_enable(int32_t enable) { g_timing = enable != 0; }
+
+int32_t beam_moe_timing_collect(double* total_ms, int32_t* launches, int32_t n_stages) {
+  for (int i = 0; i < n_stages && i < kNumStages; ++i) {
+    if (total_ms) total_ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  for (auto& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess &&
+        r.stage < n_stages) {
+      if (total_ms) total_ms[r.stage] += ms;
+      if (launches) launches[r.stage] += 1;
+    }
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_recs.clear();
+  return kNumStages;
+}
+
+const char* beam_moe_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Weighted combine with no shared expert (gfx950):
+//   out[t] = Y[t*K+0] + Y[t*K+1] + ... + Y[t*K+K-1]   (FP32, fixed k order)
+// where Y[slot] already holds topk_w[slot] * expert output (applied by the down GEMM's epilogue).
+// [V] "vLLM 实现 Reflection Beam 501B MoE 模型 Day 0 支持" §MoE and residual stream (no shared
+// expert); [H] "Reflection 发布 501B 开源模型 Beam，Apache 2.0 许可" §专家混合 (outputs combined with
+// the normalised router weights times 2.5). A bf16 output is the round-to-nearest-even of the FP32 sum.
+#include "common.h"
+
+namespace beam {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
+                                                      void* __restrict__ out, int out_bf16,
+                                                      int64_t T, int H, int K) {
+  const int64_t t = blockIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  const float* y = Y + t * K * H + c;
+  floatx4 acc = *reinterpret_cast<const floatx4*>(y);
+  for (int k = 1; k < K; ++k) acc += *reinterpret_cast<const floatx4*>(y + (int64_t)k * H);
+  if (out_bf16) {
+    u32x2 p;
+    p.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+    p.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + t * H + c) = p;
+  } else {
+    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(out) + t * H + c) = acc;
+  }
+}
+
+hipError_t launch_combine(const float* ybuf, void* out, bool out_bf16, const Shape& s,
+                          hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  dim3 grid((unsigned)s.T, (unsigned)ceil_div(s.H, 1024));
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, ybuf, out, out_bf16 ? 1 : 0, s.T,
+                     s.H, s.K);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,104 @@
+// Internal device/host helpers of the Beam MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kAlignChunk = 256;              // tokens per align chunk (one mask bit each)
+constexpr int kAlignWords = kAlignChunk / 64; // 64-bit mask words per (chunk, expert)
+
+// ---- bf16 -------------------------------------------------------------------------------------
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_round(float f) {
+  return __uint_as_float(f32_to_bf16_bits(f) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) {
+  return __uint_as_float(packed & 0xFFFF0000u);
+}
+
+// SiLU in fp32 with the full-precision exponential and an IEEE division.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ---- routing/align tables carved from the workspace ------------------------------------------
+struct AlignTables {
+  uint64_t* chunk_mask;   // [n_chunks][E][kAlignWords]  bit j: token kAlignChunk*c+j chose e
+  int32_t* chunk_base;    // [n_chunks][E]  rows of expert e in chunks before c
+  int32_t* expert_count;  // [E]
+  int32_t* expert_off;    // [E+1] exclusive prefix of counts (rows in sorted order)
+  int32_t* n_blocks;      // [1]
+  int32_t* blk_expert;    // [max_blocks]
+  int32_t* blk_row0;      // [max_blocks] first sorted row of the block
+  int32_t* blk_rows;      // [max_blocks] rows in the block (1..BM)
+  int32_t* sorted_slot;   // [T*K] slot id (t*K+k) of each sorted row
+};
+
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Upper bound on the number of row blocks when every expert's rows are split into ceil(c/BM)
+// blocks: sum_e ceil(c_e/BM) <= floor(TK/BM) + min(E, TK) + 1.
+inline int64_t max_row_blocks(int64_t TK, int64_t E, int64_t BM) {
+  int64_t nz = TK < E ? TK : E;
+  return TK / BM + nz + 1;
+}
+
+}  // namespace beam
+
+// ---- launchers (host side, defined in the .hip files) -------------------------------------------
+namespace beam {
+struct Shape {
+  int64_t T;
+  int32_t H, E, G, Gk, K, F;
+  float scale;
+};
+
+hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_router,
+                                const float* bias, float2* sb, const Shape& s, hipStream_t st);
+hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const Shape& s,
+                                hipStream_t st);
+hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
+                        hipStream_t st);
+hipError_t launch_gate_up_bf16(const uint16_t* x, const uint16_t* w_gu, uint16_t* hbuf,
+                               const AlignTables& at, const Shape& s, int64_t max_blocks,
+                               bool small, hipStream_t st);
+hipError_t launch_down_bf16(const uint16_t* hbuf, const uint16_t* w_dn, const float* topk_w,
+                            float* ybuf, const AlignTables& at, const Shape& s,
+                            int64_t max_blocks, bool small, hipStream_t st);
+hipError_t launch_gate_up_f32(const float* x, const float* w_gu, float* hbuf,
+                              const AlignTables& at, const Shape& s, int64_t max_blocks,
+                              hipStream_t st);
+hipError_t launch_down_f32(const float* hbuf, const float* w_dn, const float* topk_w, float* ybuf,
+                           const AlignTables& at, const Shape& s, int64_t max_blocks,
+                           hipStream_t st);
+hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols,
+                                 const int32_t* n_rows_dev, uint8_t* codes, float* scales,
+                                 hipStream_t st);
+hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const uint8_t* w_gu,
+                              const float* w_gu_scale, uint16_t* hbuf, const AlignTables& at,
+                              const Shape& s, int64_t max_blocks, bool small, hipStream_t st);
+hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w_dn,
+                           const float* w_dn_scale, const float* topk_w, float* ybuf,
+                           const AlignTables& at, const Shape& s, int64_t max_blocks, bool small,
+                           hipStream_t st);
+int small_block_rows();
+int tiled_block_rows();
+hipError_t launch_combine(const float* ybuf, void* out, bool out_bf16, const Shape& s,
+                          hipStream_t st);
+}  // namespace beam

@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every symbol include/beam_moe.h declares, and rejects bad
+arguments with the documented status before any launch (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_grouped_expert_fp32_amd as bm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "beam_moe.h")
+
+OK, NULL, ALIGN, SHAPE, DTYPE, UNSUP, WS, ALIAS, LAUNCH, DEVICE = range(10)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"BEAM_API\s+[\w\s\*]+?\b(beam_\w+)\s*\(", text)
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ["beam_moe_route", "beam_moe_forward", "beam_moe_workspace_bytes",
+              "beam_moe_route_workspace_bytes", "beam_status_string", "beam_moe_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bm.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.beam_moe_version() >= 100
+    for s in range(10):
+        assert bm.status_string(s) not in ("", "unknown status")
+
+
+def _cfg(**kw):
+    return bm.make_cfg(**kw)
+
+
+# fake, aligned device addresses: validation rejects the call before anything dereferences them
+A = [(i + 1) << 40 for i in range(12)]   # 1 TiB apart: no accidental overlap
+
+
+def _fwd(cfg, T=32, x=A[0], wr=A[1], bias=A[2], wgu=A[3], wd=A[4], out=A[5], gus=None, ds=None,
+         ids=None, w=None, ws=A[8], ws_bytes=1 << 38):
+    lib = bm.lib()
+    return lib.beam_moe_forward(x, wr, bias, wgu, wd, out, T,
+                                ctypes.byref(cfg) if cfg is not None else None, gus, ds, ids, w,
+                                ws, ws_bytes, None)
+
+
+def _route(cfg, T=32, x=A[0], wr=A[1], bias=A[2], ids=A[6], w=A[7], ws=A[8], ws_bytes=1 << 38):
+    return bm.lib().beam_moe_route(x, wr, bias, ids, w, T,
+                                   ctypes.byref(cfg) if cfg is not None else None, ws, ws_bytes,
+                                   None)
+
+
+def test_null_cfg_and_pointers():
+    assert _fwd(None) == NULL
+    assert _route(None) == NULL
+    c = _cfg()
+    assert _fwd(c, x=None) == NULL
+    assert _fwd(c, wd=None) == NULL
+    assert _fwd(c, ws=None) == NULL
+    assert _route(c, ids=None) == NULL
+
+
+def test_shape_errors():
+    assert _fwd(_cfg(n_groups=7)) == SHAPE                 # 256 % 7
+    assert _fwd(_cfg(topk_groups=9)) == SHAPE              # more kept groups than groups
+    assert _fwd(_cfg(topk=200)) == SHAPE                   # K > Gk * E / G
+    assert _fwd(_cfg(routed_scale=0.0)) == SHAPE
+    assert _fwd(_cfg(routed_scale=float("nan"))) == SHAPE
+    assert _fwd(_cfg(), T=-1) == SHAPE
+    assert _route(_cfg(), T=-5) == SHAPE
+
+
+def test_dtype_errors():
+    assert _fwd(_cfg(x_dtype=7)) == DTYPE
+    assert _fwd(_cfg(out_dtype=bm.BEAM_FP8_E4M3)) == DTYPE
+    assert _fwd(_cfg(x_dtype=bm.BEAM_F32, w_dtype=bm.BEAM_BF16)) == DTYPE
+    assert _fwd(_cfg(x_dtype=bm.BEAM_BF16, w_dtype=bm.BEAM_F32)) == DTYPE
+    assert _fwd(_cfg(), gus=A[9]) == DTYPE                 # scales only with fp8 weights
+
+
+def test_unsupported_shapes():
+    assert _fwd(_cfg(hidden=5000)) == UNSUP
+    assert _fwd(_cfg(d_ff=2500)) == UNSUP
+    assert _fwd(_cfg(n_experts=512, n_groups=8)) == UNSUP
+    assert _fwd(_cfg(topk=17, topk_groups=8)) == UNSUP
+
+
+def test_zero_tokens_is_a_noop():
+    assert _fwd(_cfg(), T=0) == OK
+    assert _route(_cfg(), T=0) == OK
+    assert _fwd(_cfg(), T=0, x=None, out=None, ws=None) == OK
+
+
+def test_alignment():
+    assert _fwd(_cfg(), x=A[0] + 2) == ALIGN
+    assert _fwd(_cfg(), out=A[5] + 8) == ALIGN
+    assert _fwd(_cfg(), ids=A[6] + 4) == ALIGN
+    assert _route(_cfg(), w=A[7] + 4) == ALIGN
+
+
+def test_workspace_size():
+    c = _cfg()
+    need = bm.workspace_bytes(c, 32)
+    assert need > 0
+    assert _fwd(c, ws_bytes=need - 1) == WS
+    assert bm.workspace_bytes(_cfg(n_groups=7), 32) == 0
+    rneed = bm.route_workspace_bytes(c, 32)
+    assert 0 < rneed < need
+    assert _route(c, ws_bytes=rneed - 1) == WS
+
+
+def test_aliasing():
+    c = _cfg()
+    assert _fwd(c, out=A[0]) == ALIAS                      # out on top of x
+    assert _fwd(c, out=A[8]) == ALIAS                      # out inside the workspace
+    assert _fwd(c, ids=A[5]) == ALIAS                      # routing copy on top of out
+    assert _route(c, ids=A[7], w=A[7]) == ALIAS
+
+
+def test_valid_call_without_gpu_reports_device():
+    """A fully valid call on a machine with no gfx950 device fails loudly, it never falls back."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _fwd(_cfg()) == DEVICE
+    assert _route(_cfg()) == DEVICE

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the seeded workloads.
+
+Tiny FP32 and decode (T=32) are compared on every token; prefill (T=8192) and skewed (T=32768)
+routing is compared on every token and outputs on sampled tokens, at the sizes and in the launch
+configuration the benchmark times. Ragged token counts, T = 0, determinism, untouched inputs, a
+poisoned workspace and the bf16 output copy are covered too.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+import routing_grouped_expert_fp32_amd as bm
+import synthgen
+from oracle import router
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _cfg(wl, out="f32"):
+    return bm.WorkloadCfg.of(wl.shape, wl.x_dtype, wl.w_dtype, out)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def beam_bf16():
+    """Beam-shape bf16 expert weights and router (shared by every bf16 workload), on the GPU."""
+    _say("generating Beam bf16 weights on cuda:0")
+    d = synthgen.make_inputs("prefill", device="cuda", T=1)
+    torch.cuda.synchronize()
+    return d
+
+
+def _inputs(name, weights, T=None, skew_delta=None):
+    wl = synthgen.WORKLOADS[name]
+    d = synthgen.make_inputs(wl, device="cuda", T=T, with_experts=False, skew_delta=skew_delta)
+    for k in ("w_gate_up", "w_down", "w_router"):
+        d[k] = weights[k]
+    return wl, d
+
+
+def _run(wl, d, out_dtype="f32", workspace=None):
+    cfg = _cfg(wl, out_dtype)
+    T = d["T"]
+    ids = torch.empty((T, wl.shape.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, wl.shape.topk), dtype=torch.float32, device="cuda")
+    out = bm.forward(d["x"], d["w_router"], d["bias"], d["w_gate_up"], d["w_down"], cfg,
+                     topk_ids_out=ids, topk_w_out=w, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, ids, w
+
+
+def _sample(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(pick))
+
+
+def _route_oracle(wl, d):
+    sh = wl.shape
+    return router.route(d["x"].cpu(), d["w_router"].cpu(), d["bias"].cpu(), sh.n_groups,
+                        sh.topk_groups, sh.topk, sh.routed_scale)
+
+
+def test_generator_identical_on_cpu_and_gpu():
+    for args in [((64, 512), 1.0, 0, 1, torch.float32, 0), ((8, 5120), 1.0, 0, 1, torch.bfloat16, 0),
+                 ((3, 5120), 0.02, 0, 4, torch.bfloat16, 255 * 5120 * 5120 + 7),
+                 ((2, 4096), 0.02, 0, 4, torch.bfloat16, (1 << 32) - 4096)]:
+        shape, sig, seed, tid, dt, off = args
+        a = synthgen.normal(shape, sig, seed, tid, "cpu", dt, off)
+        b = synthgen.normal(shape, sig, seed, tid, "cuda", dt, off).cpu()
+        assert torch.equal(a.view(torch.int16) if dt == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if dt == torch.bfloat16 else b.view(torch.int32))
+    ua = synthgen.uniform((256,), -0.1, 0.1, 0, 3, "cpu")
+    ub = synthgen.uniform((256,), -0.1, 0.1, 0, 3, "cuda").cpu()
+    assert torch.equal(ua.view(torch.int32), ub.view(torch.int32))
+    qa, sa = synthgen.fp8_rows(64, 5120, 0.02, 0, 4, "cpu", 12345 * 5120)
+    qb, sb = synthgen.fp8_rows(64, 5120, 0.02, 0, 4, "cuda", 12345 * 5120)
+    assert torch.equal(qa, qb.cpu()) and torch.equal(sa.view(torch.int32), sb.cpu().view(torch.int32))
+
+
+def test_tiny_fp32_all_tokens():
+    wl = synthgen.WORKLOADS["tiny"]
+    d = synthgen.make_inputs(wl, device="cuda")
+    _say("tiny fp32 forward")
+    out, ids, w = _run(wl, d)
+    r = _route_oracle(wl, d)
+    rc = parity.check_routing(ids.cpu().numpy(), w.cpu().numpy(), r)
+    assert rc["ok"], rc
+    get = parity.expert_loader(d["w_gate_up"], d["w_down"], wl.shape.d_ff)
+    err, _ = parity.check_outputs(out.cpu().numpy(), d["x"], ids.cpu().numpy(), r,
+                                  wl.shape.routed_scale, get, "fp32", np.arange(wl.T))
+    _say("tiny fp32 max|err|/rms", err)
+    assert err <= parity.TOL["f32"]
+
+
+def test_route_entry_point(beam_bf16):
+    for name, T in [("tiny", None), ("decode", None), ("decode", 1000)]:
+        if name == "tiny":
+            wl = synthgen.WORKLOADS["tiny"]
+            d = synthgen.make_inputs(wl, device="cuda", with_experts=False)
+        else:
+            wl, d = _inputs(name, beam_bf16, T=T)
+        _say("route", name, d["T"])
+        ids, w = bm.route(d["x"], d["w_router"], d["bias"], _cfg(wl))
+        torch.cuda.synchronize()
+        rc = parity.check_routing(ids.cpu().numpy(), w.cpu().numpy(), _route_oracle(wl, d))
+        assert rc["ok"], rc
+        assert np.allclose(w.sum(dim=1).cpu().numpy(), 2.5, atol=1e-6)
+
+
+def test_decode_bf16_all_tokens(beam_bf16):
+    wl, d = _inputs("decode", beam_bf16)
+    _say("decode bf16 forward T=32")
+    out, ids, w = _run(wl, d)
+    r = _route_oracle(wl, d)
+    rc = parity.check_routing(ids.cpu().numpy(), w.cpu().numpy(), r)
+    assert rc["ok"], rc
+    get = parity.expert_loader(d["w_gate_up"], d["w_down"], wl.shape.d_ff)
+    err, rms = parity.check_outputs(out.cpu().numpy(), d["x"], ids.cpu().numpy(), r,
+                                    wl.shape.routed_scale, get, "bf16", np.arange(wl.T))
+    _say("decode max|err|/rms", err, "rms", rms, "near ties", rc["near_ties"])
+    assert err <= parity.TOL["bf16"]
+
+
+def test_prefill_bf16_sampled(beam_bf16):
+    wl, d = _inputs("prefill", beam_bf16)
+    _say("prefill bf16 forward T=8192")
+    out, ids, w = _run(wl, d)
+    r = _route_oracle(wl, d)
+    rc = parity.check_routing(ids.cpu().numpy(), w.cpu().numpy(), r)
+    _say("prefill routing", {k: (len(v) if isinstance(v, list) else v) for k, v in rc.items()})
+    assert rc["ok"], rc
+    toks = _sample(wl.T, 12, seed=1)
+    get = parity.expert_loader(d["w_gate_up"], d["w_down"], wl.shape.d_ff)
+    err, _ = parity.check_outputs(out.cpu().numpy()[toks], d["x"], ids.cpu().numpy(), r,
+                                  wl.shape.routed_scale, get, "bf16", toks)
+    _say("prefill sampled max|err|/rms", err)
+    assert err <= parity.TOL["bf16"]
+    assert torch.isfinite(out).all()
+
+
+def test_skew_bf16_sampled(beam_bf16):
+    delta = json.load(open(os.path.join(GOLD, "skew_bias.json")))["delta"]
+    wl, d = _inputs("skew", beam_bf16, skew_delta=delta)
+    _say("skew bf16 forward T=32768")
+    out, ids, w = _run(wl, d)
+    r = _route_oracle(wl, d)
+    rc = parity.check_routing(ids.cpu().numpy(), w.cpu().numpy(), r)
+    _say("skew routing", {k: (len(v) if isinstance(v, list) else v) for k, v in rc.items()})
+    assert rc["ok"], rc
+    hot = synthgen.hot_set(16, 256, 0)
+    frac = np.isin(ids.cpu().numpy(), hot).mean()
+    assert abs(frac - 0.40) < 0.006
+    toks = _sample(wl.T, 8, seed=2)
+    get = parity.expert_loader(d["w_gate_up"], d["w_down"], wl.shape.d_ff)
+    err, _ = parity.check_outputs(out.cpu().numpy()[toks], d["x"], ids.cpu().numpy(), r,
+                                  wl.shape.routed_scale, get, "bf16", toks)
+    _say("skew sampled max|err|/rms", err)
+    assert err <= parity.TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [1, 3, 77, 129, 300])
+def test_ragged_token_counts(beam_bf16, T):
+    wl, d = _inputs("decode", beam_bf16, T=T)
+    _say("ragged decode-shape forward T =", T)
+    out, ids, w = _run(wl, d)
+    r = _route_oracle(wl, d)
+    rc = parity.check_routing(ids.cpu().numpy(), w.cpu().numpy(), r)
+    assert rc["ok"], rc
+    toks = _sample(T, 10, seed=T)
+    get = parity.expert_loader(d["w_gate_up"], d["w_down"], wl.shape.d_ff)
+    err, _ = parity.check_outputs(out.cpu().numpy()[toks], d["x"], ids.cpu().numpy(), r,
+                                  wl.shape.routed_scale, get, "bf16", toks)
+    _say("ragged", T, "max|err|/rms", err)
+    assert err <= parity.TOL["bf16"]
+
+
+def test_zero_tokens(beam_bf16):
+    wl, d = _inputs("decode", beam_bf16, T=0)
+    out = bm.forward(d["x"], d["w_router"], d["bias"], d["w_gate_up"], d["w_down"], _cfg(wl))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 5120)
+
+
+def test_determinism_untouched_inputs_poisoned_workspace(beam_bf16):
+    for T in (32, 2048):
+        wl, d = _inputs("decode", beam_bf16, T=T)
+        _say("determinism T =", T)
+        sums = {k: d[k].view(torch.uint8)[: 1 << 24].sum().item() for k in ("x", "bias")}
+        gu_probe = d["w_gate_up"][7, :4].clone()
+        ws = torch.empty(bm.workspace_bytes(_cfg(wl), T), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)                                   # NaN bytes everywhere
+        out1, ids1, w1 = _run(wl, d, workspace=ws)
+        ws.fill_(0x7F)
+        out2, ids2, w2 = _run(wl, d, workspace=ws)
+        assert torch.equal(out1, out2) and torch.equal(ids1, ids2) and torch.equal(w1, w2)
+        assert torch.isfinite(out1).all()
+        for k, v in sums.items():
+            assert d[k].view(torch.uint8)[: 1 << 24].sum().item() == v
+        assert torch.equal(d["w_gate_up"][7, :4], gu_probe)
+
+
+def test_bf16_output_is_rounded_fp32_output(beam_bf16):
+    wl, d = _inputs("decode", beam_bf16)
+    out32, _, _ = _run(wl, d, "f32")
+    out16, _, _ = _run(wl, d, "bf16")
+    assert out16.dtype == torch.bfloat16
+    assert torch.equal(out16.view(torch.int16), out32.to(torch.bfloat16).view(torch.int16))
