@@ -1,0 +1,233 @@
+"""Benchmark of the Beam routed-MoE block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skew]
+                    [--also prefill] [--no-cpu-baseline]
+
+A step is one beam_moe_forward over one batch (router, selection, moe_align, gate/up GEMM, down
+GEMM, combine), inputs already resident in HBM. The timed region is bracketed by
+torch.cuda.synchronize() on both sides; per-stage HIP events recorded by the library on the
+call's stream during the same timed steps give each kernel's average duration. Prints ONE JSON
+line.
+
+roofline (dominant kernel = the gate/up grouped GEMM): algorithmic bytes per launch =
+  distinct experts touched (counted from the routing of the batch) * 2 * d_ff * hidden * 2 B
+  (the gate and up weights, read once) + T * hidden * 2 B (x, read once) + T * K * d_ff * 2 B
+(h written once), divided by the kernel's average duration. Each weight byte (bf16) feeds one
+multiply-add per routed row, so the kernel's FLOP per weight byte equals the rows per expert
+T*K/E: below the bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312) the bound is "hbm", else "mfma" with
+algorithmic FLOP = 2 * T * K * 2 * d_ff * hidden.
+traffic: FETCH_SIZE + WRITE_SIZE of the kernel from rocprofv3 --pmc runs recorded in
+profiles/counters_<workload>.json, scaled by the same counters on a plain copy; null if that file
+is missing or was taken on a different version of the kernel source.
+cpu_baseline: the CPU oracle (float64 numpy) on a bounded sample of the same batch (routing of the
+whole batch + expert MLPs and combine for the first --cpu-tokens tokens), on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "common.h"):
+        with open(os.path.join(ROOT, "routing_grouped_expert_fp32_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew"])
+    p.add_argument("--also", default="prefill", help="comma list of extra workloads ('' = none)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=4)
+    p.add_argument("--copy-probe-gib", type=float, default=0.0,
+                   help="also run a plain device copy of this size (counter scaling reference)")
+    return p.parse_args()
+
+
+def skew_delta():
+    with open(os.path.join(ROOT, "tests", "golden", "skew_bias.json")) as f:
+        return json.load(f)["delta"]
+
+
+def measure(bm, synthgen, torch, name, weights, steps, warmup):
+    wl = synthgen.WORKLOADS[name]
+    d = synthgen.make_inputs(wl, device="cuda", with_experts=False,
+                             skew_delta=skew_delta() if name == "skew" else None)
+    sh = wl.shape
+    cfg = bm.WorkloadCfg.of(sh, wl.x_dtype, wl.w_dtype)
+    T = wl.T
+    ws = torch.empty(bm.workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, sh.topk), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bm.forward(d["x"], weights["w_router"], d["bias"], weights["w_gate_up"],
+                   weights["w_down"], cfg, out=out, topk_ids_out=ids, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    bm.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    bm.timing_enable(False)
+    stages = bm.timing_collect()
+    distinct = int(torch.unique(ids).numel())
+    F, H, K = sh.d_ff, sh.hidden, sh.topk
+    gu_ms = stages["gate_up"][0] / max(stages["gate_up"][1], 1)
+    gu_bytes = distinct * 2 * F * H * 2 + T * H * 2 + T * K * F * 2
+    gu_flops = 2.0 * T * K * 2 * F * H
+    rows_per_expert = T * K / sh.n_experts
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    layer_bytes = distinct * 3 * F * H * 2 + sh.n_experts * H * 4 + sh.n_experts * 4 + T * H * 2 \
+        + T * H * 4
+    layer_flops = 2.0 * T * K * 3 * F * H
+    ms = elapsed * 1e3 / steps
+    res = {
+        "workload": name, "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+        "layer_TBps": layer_bytes / (ms * 1e-3) / 1e12, "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
+        "distinct_experts": distinct,
+        "stages_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items()},
+        "gate_up": {"ms": gu_ms, "bytes": gu_bytes, "flops": gu_flops,
+                    "GBps": gu_bytes / (gu_ms * 1e-3) / 1e9,
+                    "TFLOPs": gu_flops / (gu_ms * 1e-3) / 1e12},
+        "bound": "hbm" if rows_per_expert < ridge else "mfma",
+    }
+    del ws, out
+    return res, d, ids
+
+
+def roofline(r, workload):
+    g = r["gate_up"]
+    if r["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": g["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": g["GBps"] / HBM_PEAK_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": g["TFLOPs"] / BF16_PEAK_TFLOPS}
+    roof["kernel"] = "gate_up (grouped_%s_kernel<true>)" % ("small" if r["T"] * 8 <= 1024 else
+                                                            "tiled")
+    roof["algorithmic_bytes_per_launch"] = g["bytes"]
+    roof["traffic"] = None
+    cpath = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if os.path.exists(cpath):
+        with open(cpath) as f:
+            c = json.load(f)
+        if c.get("kernel_source_hash") == kernel_source_hash():
+            roof["traffic"] = c.get("gate_up_hbm_bytes_per_launch")
+    return roof
+
+
+def cpu_baseline(torch, synthgen, d, weights, ids_gpu, wl_name, n_tok):
+    """The oracle as it stands, on the host cores: full-batch routing plus the expert MLPs and
+    combine of the first n_tok tokens (their experts' weights copied to the host beforehand)."""
+    import numpy as np
+    from oracle import experts, router
+    wl = synthgen.WORKLOADS[wl_name]
+    sh = wl.shape
+    x_h, wr_h, b_h = d["x"].cpu(), weights["w_router"].cpu(), d["bias"].cpu()
+    toks = list(range(n_tok))
+    r0 = router.route(x_h[:n_tok], wr_h, b_h, sh.n_groups, sh.topk_groups, sh.topk, sh.routed_scale)
+    need = sorted(set(int(e) for e in r0.ids.ravel()))
+    host_w = {e: (weights["w_gate_up"][e].cpu(), weights["w_down"][e].cpu()) for e in need}
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    t0 = time.perf_counter()
+    r = router.route(x_h, wr_h, b_h, sh.n_groups, sh.topk_groups, sh.topk, sh.routed_scale)
+    t_route = time.perf_counter() - t0
+    get = lambda e: experts.split_expert(host_w[e][0], host_w[e][1], sh.d_ff)  # noqa: E731
+    t1 = time.perf_counter()
+    experts.forward_expert_major(x_h[:n_tok], r.ids[toks], r.weights[toks], get, "bf16")
+    t_exp = time.perf_counter() - t1
+    # per-token cost of the whole block: routing amortised over the batch + experts per token
+    per_tok = t_route / wl.T + t_exp / n_tok
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": int(max(blas,
+                                                                          torch.get_num_threads())),
+            "kind": "oracle",
+            "sample": f"{wl_name}: routing of all {wl.T} tokens ({t_route:.2f} s) + expert MLPs and "
+                      f"combine of {n_tok} tokens / {n_tok * sh.topk} expert calls ({t_exp:.2f} s), "
+                      f"float64 numpy"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this build has no "
+              "multi-GPU path; see DESIGN.md for how the block would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import routing_grouped_expert_fp32_amd as bm
+    import synthgen
+    bm.lib()
+    torch.cuda.set_device(0)
+    print(f"[bench] generating Beam bf16 weights on {torch.cuda.get_device_name(0)}",
+          file=sys.stderr, flush=True)
+    weights = synthgen.make_inputs("prefill", device="cuda", T=1)
+    torch.cuda.synchronize()
+    main_res, d, ids = measure(bm, synthgen, torch, a.workload, weights, a.steps, a.warmup)
+    print(f"[bench] {a.workload}: {main_res['ms_per_step']:.3f} ms/step", file=sys.stderr,
+          flush=True)
+    extra = {}
+    for name in [s for s in a.also.split(",") if s and s != a.workload]:
+        r, _, _ = measure(bm, synthgen, torch, name, weights, max(5, a.steps // 2), a.warmup)
+        r["roofline"] = roofline(r, name)
+        extra[name] = r
+        print(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    if a.copy_probe_gib > 0:
+        n = int(a.copy_probe_gib * 2 ** 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(torch, synthgen, d, weights, ids, a.workload, a.cpu_tokens)
+    wl = synthgen.WORKLOADS[a.workload]
+    sh = wl.shape
+    line = {
+        "metric": "MoE-layer tokens/sec (d5120, 256 exp, top-8); % of roofline",
+        "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{a.workload}: Beam MoE layer, T={wl.T}, hidden {sh.hidden}, "
+                               f"{sh.n_experts} experts ({sh.n_groups} groups, keep "
+                               f"{sh.topk_groups}), top-{sh.topk}, d_ff {sh.d_ff}, bf16 experts, "
+                               f"FP32 router, fp32 out",
+                   "T": wl.T, "global_batch": wl.T, "parallelism": "single GPU"},
+        "roofline": roofline(main_res, a.workload),
+        "cpu_baseline": cpu,
+        "detail": main_res,
+        "also": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

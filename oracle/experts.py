@@ -25,6 +25,7 @@ from typing import Callable
 import numpy as np
 
 from .codecs import bf16_round, e4m3_decode, quant_rows_fp8
+from .router import to_f64
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -38,7 +39,7 @@ def expert_mlp(x_rows: np.ndarray, ex: dict, contract: str) -> np.ndarray:
     these are the *decoded codes* and `ex` also holds "gate_scale" [F], "up_scale" [F],
     "down_scale" [H]. For the fp8 contract x_rows must be the bf16 token values (float64 copies).
     """
-    x = np.asarray(x_rows, dtype=np.float64)
+    x = to_f64(x_rows)
     if contract == "fp32":
         g = x @ ex["gate"].T
         u = x @ ex["up"].T
@@ -76,7 +77,7 @@ def forward_expert_major(x, ids, w, get_expert: Callable[[int], dict], contract:
     Groups the (token, k) slots by expert, runs each expert once on its rows, scatters
     w * y back to the slots and combines. get_expert(e) returns the dict expert_mlp expects.
     """
-    x = np.asarray(x, dtype=np.float64)
+    x = to_f64(x)
     ids = np.asarray(ids)
     w = np.asarray(w, dtype=np.float64)
     T, K = ids.shape
@@ -93,7 +94,7 @@ def forward_expert_major(x, ids, w, get_expert: Callable[[int], dict], contract:
 
 def forward_token_major(x, ids, w, get_expert: Callable[[int], dict], contract: str):
     """Same result as forward_expert_major, computed one token and one expert at a time."""
-    x = np.asarray(x, dtype=np.float64)
+    x = to_f64(x)
     T, K = np.asarray(ids).shape
     out = None
     for t in range(T):
