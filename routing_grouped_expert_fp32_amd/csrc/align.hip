@@ -7,9 +7,9 @@
 //                    of the chunk chose it (LDS 64-bit atomic OR); popcounts give chunk counts.
 //   2. align_scan    (one WG of 1024 threads): per expert, exclusive prefix over chunks, expert
 //                    totals and offsets, and the row-block table: an expert with c rows gets
-//                    ceil(c/BM) blocks of near-equal size (sizes differ by at most one row), so a
-//                    block never carries more than BM-1 rows of padding and skewed experts split
-//                    into many equal blocks.
+//                    floor(c/BM) full blocks of BM rows and one block with the remainder, so
+//                    skewed experts split into many full blocks and only the last block of an
+//                    expert is partly filled (the GEMMs skip its empty 16-row sub-tiles).
 //   3. align_scatter (one WG per chunk): each slot's row = expert offset + chunk base + number of
 //                    earlier tokens of the chunk that chose the same expert (popcount of the mask
 //                    below the token's bit). Rows of an expert are therefore in token order — a
@@ -134,13 +134,10 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* __restrict__ 
       expert_off[E] = scan_rows[e];
       n_blocks[0] = scan_blks[e];
     }
-    if (nb > 0) {
-      const int q = count / nb, rem = count % nb;
-      for (int i = 0; i < nb; ++i) {
-        blk_expert[blk_start + i] = e;
-        blk_row0[blk_start + i] = row_start + i * q + (i < rem ? i : rem);
-        blk_rows[blk_start + i] = q + (i < rem ? 1 : 0);
-      }
+    for (int i = 0; i < nb; ++i) {   // full blocks of BM rows, then the remainder
+      blk_expert[blk_start + i] = e;
+      blk_row0[blk_start + i] = row_start + i * BM;
+      blk_rows[blk_start + i] = min(BM, count - i * BM);
     }
   }
 }

@@ -19,6 +19,7 @@
 // Row blocks come from moe_align: (expert, first sorted row, rows). Grids are sized by an upper
 // bound on the block count; blocks past the device-side count exit at once (no host readback).
 #include "common.h"
+#include "gemm_pipe.h"
 
 namespace beam {
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void grouped_tiled_kernel(const uint16_t* _
 }
 
 int small_block_rows() { return kSmallBM; }
-int tiled_block_rows() { return kTBM; }
+int tiled_block_rows() { return kPBM; }
 
 hipError_t launch_gate_up_bf16(const uint16_t* x, const uint16_t* w_gu, uint16_t* hbuf,
                                const AlignTables& at, const Shape& s, int64_t max_blocks,
@@ -241,9 +242,10 @@ hipError_t launch_gate_up_bf16(const uint16_t* x, const uint16_t* w_gu, uint16_t
     hipLaunchKernelGGL((grouped_small_kernel<true>), grid, dim3(256), 0, st, x, w_gu, nullptr,
                        hbuf, at, s.H, s.F, s.K);
   } else {
-    dim3 grid(s.F / 64, (unsigned)max_blocks);
-    hipLaunchKernelGGL((grouped_tiled_kernel<true>), grid, dim3(256), 0, st, x, w_gu, nullptr,
-                       hbuf, at, s.H, s.F, s.K);
+    const int n_ctiles = s.F / 128;
+    const int64_t wgs = 8 * ceil_div(max_blocks * n_ctiles, 8);
+    hipLaunchKernelGGL((grouped_pipe_kernel<true>), dim3((unsigned)wgs), dim3(256), 0, st, x,
+                       w_gu, nullptr, hbuf, at, s.H, s.F, s.K, n_ctiles);
   }
   return hipGetLastError();
 }
@@ -257,9 +259,10 @@ hipError_t launch_down_bf16(const uint16_t* hbuf, const uint16_t* w_dn, const fl
     hipLaunchKernelGGL((grouped_small_kernel<false>), grid, dim3(256), 0, st, hbuf, w_dn, topk_w,
                        ybuf, at, s.F, s.H, s.K);
   } else {
-    dim3 grid(s.H / kTBN, (unsigned)max_blocks);
-    hipLaunchKernelGGL((grouped_tiled_kernel<false>), grid, dim3(256), 0, st, hbuf, w_dn, topk_w,
-                       ybuf, at, s.F, s.H, s.K);
+    const int n_ctiles = s.H / 256;
+    const int64_t wgs = 8 * ceil_div(max_blocks * n_ctiles, 8);
+    hipLaunchKernelGGL((grouped_pipe_kernel<false>), dim3((unsigned)wgs), dim3(256), 0, st, hbuf,
+                       w_dn, topk_w, ybuf, at, s.F, s.H, s.K, n_ctiles);
   }
   return hipGetLastError();
 }
