@@ -129,6 +129,16 @@ BEAM_API beam_status_t beam_moe_forward(const void* x, const float* w_router, co
                                void* stream);
 BEAM_API size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int64_t T);
 
+/* Dynamic FP8 E4M3 quantisation of bf16 rows, the activation step of the FP8 experts (dynamic FP8
+ * checkpoints: [S] §Highlights, §BF16, NVFP4 and FP8 Model Support).
+ *   src    [rows][cols] bf16 (device), cols % 8 == 0
+ *   codes  [rows][cols] uint8 out: OCP E4M3FN codes of v * (448 / amax_row), rounded to nearest even
+ *          and saturated to +-448; the sign of zero follows the input
+ *   scales [rows] fp32 out: amax_row / 448 (1 for an all-zero row, whose codes are all 0)
+ * amax, the scale and the product are taken in FP32 with correctly rounded operations. */
+BEAM_API beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols,
+                                          uint8_t* codes, float* scales, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 BEAM_API const char* beam_status_string(beam_status_t status);
 

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "BEAM_F32", "BEAM_BF16", "BEAM_FP8_E4M3", "Cfg", "make_cfg", "lib", "lib_path", "route",
     "forward", "workspace_bytes", "route_workspace_bytes", "BeamError", "timing_enable",
-    "timing_collect", "STAGES", "status_string",
+    "timing_collect", "STAGES", "status_string", "quant_fp8",
 ]
 
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_timing_collect.restype = i32
         L.beam_moe_stage_name.argtypes = [i32]
         L.beam_moe_stage_name.restype = ctypes.c_char_p
+        L.beam_moe_quant_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
+        L.beam_moe_quant_fp8.restype = i32
         _LIB = L
     return _LIB
 
@@ -162,6 +164,21 @@ def forward(x, w_router, bias, w_gate_up, w_down, cfg: Cfg, out=None, w_gate_up_
     if rc != 0:
         raise BeamError(rc, "beam_moe_forward")
     return out
+
+
+def quant_fp8(src, codes=None, scales=None, stream=None):
+    """beam_moe_quant_fp8 on bf16 rows src [rows][cols]: returns (codes uint8, scales fp32)."""
+    rows, cols = src.shape
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=src.device)
+    _check_dev(src, codes, scales)
+    rc = lib().beam_moe_quant_fp8(_ptr(src), rows, cols, _ptr(codes), _ptr(scales),
+                                  _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_quant_fp8")
+    return codes, scales
 
 
 def timing_enable(on: bool = True) -> None:

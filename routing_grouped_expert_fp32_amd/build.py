@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbeam_moe.so")
-SOURCES = ["api.cpp", "router.hip", "align.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip"]
+SOURCES = ["api.cpp", "router.hip", "align.hip", "gemm_grouped.hip", "gemm_f32.hip", "fp8.hip",
+           "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -110,7 +110,6 @@ beam_status_t check_cfg(const beam_moe_cfg* c, bool experts) {
   if (experts) {
     if (c->d_ff % 256 != 0 || (int64_t)c->hidden * c->d_ff >= (int64_t(1) << 31))
       return BEAM_ERR_UNSUPPORTED;
-    if (c->w_dtype == BEAM_FP8_E4M3) return BEAM_ERR_UNSUPPORTED;  // not in this build yet
   }
   return BEAM_OK;
 }
@@ -329,15 +328,46 @@ beam_status_t beam_moe_forward(const void* x, const float* w_router, const float
                                        L.max_blocks, st));
     LAUNCH(6, beam::launch_down_f32(hbuf, reinterpret_cast<const float*>(w_down), tw, ybuf, at, s,
                                     L.max_blocks, st));
+  } else if (!fp8) {
+    uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
+    LAUNCH(4, beam::launch_gate_up(x, w_gate_up, hbuf, nullptr, nullptr, false, at, s,
+                                   L.max_blocks, small, st));
+    LAUNCH(6, beam::launch_down(hbuf, w_down, nullptr, nullptr, false, tw, ybuf, at, s,
+                                L.max_blocks, small, st));
   } else {
     uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
-    LAUNCH(4, beam::launch_gate_up_bf16(reinterpret_cast<const uint16_t*>(x),
-                                        reinterpret_cast<const uint16_t*>(w_gate_up), hbuf, at, s,
-                                        L.max_blocks, small, st));
-    LAUNCH(6, beam::launch_down_bf16(hbuf, reinterpret_cast<const uint16_t*>(w_down), tw, ybuf,
-                                     at, s, L.max_blocks, small, st));
+    uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+    float* xs = reinterpret_cast<float*>(ws + L.xs);
+    uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+    float* hs = reinterpret_cast<float*>(ws + L.hs);
+    LAUNCH(3, beam::launch_quant_rows_fp8(reinterpret_cast<const uint16_t*>(x), T, c.hidden, xq, xs,
+                                          st));
+    LAUNCH(4, beam::launch_gate_up(xq, w_gate_up, hbuf, xs, w_gate_up_scale, true, at, s,
+                                   L.max_blocks, small, st));
+    LAUNCH(5, beam::launch_quant_rows_fp8(hbuf, T * c.topk, c.d_ff, hq, hs, st));
+    LAUNCH(6, beam::launch_down(hq, w_down, hs, w_down_scale, true, tw, ybuf, at, s, L.max_blocks,
+                                small, st));
   }
   LAUNCH(7, beam::launch_combine(ybuf, out, c.out_dtype == BEAM_BF16, s, st));
+  return BEAM_OK;
+}
+
+beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols, uint8_t* codes,
+                                 float* scales, void* stream) {
+  if (rows < 0 || cols <= 0) return BEAM_ERR_SHAPE;
+  if (cols % 8 != 0 || rows >= (int64_t(1) << 31)) return BEAM_ERR_UNSUPPORTED;
+  if (rows == 0) return BEAM_OK;
+  if (!src || !codes || !scales) return BEAM_ERR_NULL;
+  if (!aligned16(src) || !aligned16(codes) || !aligned16(scales)) return BEAM_ERR_ALIGN;
+  const size_t n = (size_t)rows * (size_t)cols;
+  if (any_alias({rng(src, 2 * n)}, {rng(codes, n), rng(scales, sizeof(float) * (size_t)rows)}))
+    return BEAM_ERR_ALIAS;
+  beam_status_t rc = check_device();
+  if (rc != BEAM_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (beam::launch_quant_rows_fp8(reinterpret_cast<const uint16_t*>(src), rows, cols, codes, scales,
+                                  st) != hipSuccess)
+    return BEAM_ERR_LAUNCH;
   return BEAM_OK;
 }
 

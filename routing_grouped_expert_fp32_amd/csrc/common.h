@@ -75,28 +75,22 @@ hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const 
                                 hipStream_t st);
 hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
                         hipStream_t st);
-hipError_t launch_gate_up_bf16(const uint16_t* x, const uint16_t* w_gu, uint16_t* hbuf,
-                               const AlignTables& at, const Shape& s, int64_t max_blocks,
-                               bool small, hipStream_t st);
-hipError_t launch_down_bf16(const uint16_t* hbuf, const uint16_t* w_dn, const float* topk_w,
-                            float* ybuf, const AlignTables& at, const Shape& s,
-                            int64_t max_blocks, bool small, hipStream_t st);
+// bf16 or FP8 experts; FP8 needs the activation scales (per token for x, per sorted row for h)
+// and the per-output-channel weight scales.
+hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const float* x_scale,
+                          const float* w_scale, bool fp8, const AlignTables& at, const Shape& s,
+                          int64_t max_blocks, bool small, hipStream_t st);
+hipError_t launch_down(const void* h, const void* w_dn, const float* h_scale, const float* w_scale,
+                       bool fp8, const float* topk_w, float* ybuf, const AlignTables& at,
+                       const Shape& s, int64_t max_blocks, bool small, hipStream_t st);
 hipError_t launch_gate_up_f32(const float* x, const float* w_gu, float* hbuf,
                               const AlignTables& at, const Shape& s, int64_t max_blocks,
                               hipStream_t st);
 hipError_t launch_down_f32(const float* hbuf, const float* w_dn, const float* topk_w, float* ybuf,
                            const AlignTables& at, const Shape& s, int64_t max_blocks,
                            hipStream_t st);
-hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols,
-                                 const int32_t* n_rows_dev, uint8_t* codes, float* scales,
-                                 hipStream_t st);
-hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const uint8_t* w_gu,
-                              const float* w_gu_scale, uint16_t* hbuf, const AlignTables& at,
-                              const Shape& s, int64_t max_blocks, bool small, hipStream_t st);
-hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w_dn,
-                           const float* w_dn_scale, const float* topk_w, float* ybuf,
-                           const AlignTables& at, const Shape& s, int64_t max_blocks, bool small,
-                           hipStream_t st);
+hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
+                                 float* scales, hipStream_t st);
 int small_block_rows();
 int tiled_block_rows();
 hipError_t launch_combine(const float* ybuf, void* out, bool out_bf16, const Shape& s,

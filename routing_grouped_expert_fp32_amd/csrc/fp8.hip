@@ -1,0 +1,79 @@
+// Dynamic FP8 E4M3 quantisation of activation rows (gfx950).
+//
+// [S] "SGLang 原生支持 Reflection 的 Beam 并驱动其生产 API" §Highlights and §BF16, NVFP4 and FP8 Model
+// Support (compressed-tensors dynamic FP8 checkpoints); the format is OCP E4M3FN (largest finite
+// 448, no infinities), gfx950's native FP8 operand format.
+// Per row of bf16 values v (x per token before gate/up, h per sorted row before down):
+//   amax = max |v| (exact); scale = amax / 448, inv = 448 / amax (FP32, correctly rounded);
+//   code = E4M3(v * inv) rounded to nearest even and saturated to +-448; amax = 0 gives scale 1 and
+//   all-zero codes. The encoder is written out in integer arithmetic so the codes do not depend on
+//   any hardware conversion mode; the sign of zero follows the input (-0 -> 0x80).
+#include "common.h"
+
+namespace beam {
+
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a < 464.0f)) return sign | 0x7Eu;        // at or past 464 every rounding exceeds 448
+  if (a < 0.015625f) {                           // below 2^-6: subnormal grid of step 2^-9
+    const uint32_t m = (uint32_t)__float2int_rn(a * 512.0f);   // exact scaling, RNE to integer
+    return sign | m;                             // m = 8 is the smallest normal (0x08)
+  }
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);              // round the fp32 mantissa to 3 bits, ties to even
+  const uint32_t exp = (u >> 23) - 127u + 7u;    // E4M3 biased exponent (>= 1 here)
+  const uint32_t man = (u >> 20) & 7u;
+  if (exp > 15u || (exp == 15u && man == 7u)) return sign | 0x7Eu;   // rounded past 448
+  return sign | (exp << 3) | man;
+}
+
+// one workgroup per row; cols % 8 == 0 (8 values = one 16-byte load)
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __restrict__ src,
+                                                             int cols, uint8_t* __restrict__ codes,
+                                                             float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* p = src + row * cols;
+  const int n8 = cols >> 3;
+  float amax = 0.f;
+  for (int c = threadIdx.x; c < n8; c += 256) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p + 8 * c);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const bool zero = !(amax > 0.f);
+  const float inv = zero ? 0.f : __fdiv_rn(448.0f, amax);
+  if (threadIdx.x == 0) scales[row] = zero ? 1.0f : __fdiv_rn(amax, 448.0f);
+  for (int c = threadIdx.x; c < n8; c += 256) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p + 8 * c);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t out[2] = {0u, 0u};
+    if (!zero) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = e4m3_rne_sat(bf16_lo(w[i]) * inv);
+        const uint32_t hi = e4m3_rne_sat(bf16_hi(w[i]) * inv);
+        out[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+      }
+    }
+    *reinterpret_cast<u32x2*>(codes + row * cols + 8 * c) = u32x2{out[0], out[1]};
+  }
+}
+
+hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
+                                 float* scales, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, st, src, cols,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace beam

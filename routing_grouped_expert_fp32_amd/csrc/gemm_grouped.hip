@@ -1,0 +1,69 @@
+// Grouped expert GEMMs (gfx950): launchers for the bf16 and FP8 E4M3 experts.
+//
+// Sources: [H] "Reflection 发布 501B 开源模型 Beam，Apache 2.0 许可" §专家混合 (SwiGLU experts,
+// d_ff 2560); [S] "SGLang 原生支持 Reflection 的 Beam 并驱动其生产 API" §BF16 MoE Kernel Optimization
+// (separate decode and prefill tilings; gate/up and activation rounded to bf16; FP32 routing weight
+// applied to the down output before rounding) and §BF16, NVFP4 and FP8 Model Support (dynamic FP8).
+//
+// Operand layout: every operand row runs along the contracted dimension (x rows along H, weight rows
+// along H or F), so a lane's consecutive bytes of one row are exactly its MFMA fragment for the
+// token operand (A) and the weight operand (B) alike; D holds rows 4*(l/16)+i, column l % 16.
+// Row blocks come from moe_align: (expert, first sorted row, rows). Grids are sized by an upper
+// bound on the block count; blocks past the device-side count exit at once (no host readback).
+//   small blocks (<= 16 rows, decode): grouped_small_kernel, weights streamed into registers.
+//   large blocks (<= 256 rows, prefill): grouped_pipe_kernel, LDS ring fed by direct loads.
+#include "common.h"
+#include "gemm_pipe.h"
+#include "gemm_small.h"
+
+namespace beam {
+
+int small_block_rows() { return kSmallBM; }
+int tiled_block_rows() { return kPBM; }
+
+template <bool GATE_UP, bool FP8>
+static void launch_one(const void* a, const void* w, const float* topk_w, void* out,
+                       const float* a_scale, const float* w_scale, const AlignTables& at,
+                       int Kd, int Nout, int topk, int64_t max_blocks, bool small,
+                       hipStream_t st) {
+  const auto* A = reinterpret_cast<const unsigned char*>(a);
+  const auto* W = reinterpret_cast<const unsigned char*>(w);
+  if (small) {
+    dim3 grid(Nout / kSmallCols, (unsigned)max_blocks);
+    hipLaunchKernelGGL((grouped_small_kernel<GATE_UP, FP8>), grid, dim3(256), 0, st, A, W, topk_w,
+                       out, at, Kd, Nout, topk, a_scale, w_scale);
+  } else {
+    const int n_ctiles = GATE_UP ? Nout / 128 : Nout / 256;
+    const int64_t wgs = 8 * ceil_div(max_blocks * n_ctiles, 8);
+    hipLaunchKernelGGL((grouped_pipe_kernel<GATE_UP, FP8>), dim3((unsigned)wgs), dim3(256), 0, st,
+                       A, W, topk_w, out, at, Kd, Nout, topk, n_ctiles, a_scale, w_scale);
+  }
+}
+
+hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const float* x_scale,
+                          const float* w_scale, bool fp8, const AlignTables& at, const Shape& s,
+                          int64_t max_blocks, bool small, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (fp8)
+    launch_one<true, true>(x, w_gu, nullptr, hbuf, x_scale, w_scale, at, s.H, s.F, s.K,
+                           max_blocks, small, st);
+  else
+    launch_one<true, false>(x, w_gu, nullptr, hbuf, nullptr, nullptr, at, s.H, s.F, s.K,
+                            max_blocks, small, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_down(const void* h, const void* w_dn, const float* h_scale, const float* w_scale,
+                       bool fp8, const float* topk_w, float* ybuf, const AlignTables& at,
+                       const Shape& s, int64_t max_blocks, bool small, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (fp8)
+    launch_one<false, true>(h, w_dn, topk_w, ybuf, h_scale, w_scale, at, s.F, s.H, s.K,
+                            max_blocks, small, st);
+  else
+    launch_one<false, false>(h, w_dn, topk_w, ybuf, nullptr, nullptr, at, s.F, s.H, s.K,
+                             max_blocks, small, st);
+  return hipGetLastError();
+}
+
+}  // namespace beam

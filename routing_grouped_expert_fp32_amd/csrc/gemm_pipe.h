@@ -1,15 +1,16 @@
-// Pipelined grouped bf16 GEMM for large row blocks (gfx950): direct-to-LDS loads.
+// Pipelined grouped GEMM for large row blocks (gfx950): direct-to-LDS loads, bf16 or FP8 E4M3.
 //
 // Used by the gate/up (fused SwiGLU epilogue) and down (weighted epilogue) steps when experts carry
 // many rows (prefill-sized batches). Design:
 //   * WG tile: up to 256 rows of one expert x 256 weight columns (gate/up: 128 gate columns and the
-//     128 matching up columns); 4 waves in a 2 x 2 grid, wave tile 128 x 128 (8 x 8 MFMA
-//     16x16x32 tiles, 256 fp32 accumulators per lane).
-//   * K is staged kPBK deep. Global -> LDS with global_load_lds_dwordx4: one wave instruction lands
-//     1 KB contiguously in LDS = kPRowsPerLoad rows x kPBK*2 bytes (8 rows x 128 B at kPBK = 64, so
-//     every instruction reads whole 128-byte lines); each lane fetches the 16-byte chunk that
-//     belongs at its LDS slot. Chunk c of row r is stored at chunk position c ^ swz(r), so the 16
-//     rows a fragment read touches fall on distinct banks.
+//     128 matching up columns); 4 waves in a 2 x 2 grid, wave tile 128 x 128 (8 x 8 MFMA tiles of
+//     16 x 16, 256 fp32 accumulators per lane). bf16 uses v_mfma_f32_16x16x32_bf16, FP8 the
+//     16x16x128 f8f6f4 MFMA with unit block scales (operands OCP E4M3FN).
+//   * Each stage carries 128 bytes of every row (64 bf16 or 128 FP8 values). Global -> LDS with
+//     global_load_lds_dwordx4: one wave instruction lands 1 KB = 8 rows x 128 B (whole cache
+//     lines) contiguously in LDS; each lane fetches the 16-byte chunk that belongs at its LDS slot.
+//     Chunk c of row r is stored at chunk position c ^ (r & 7), so the 16 rows a fragment read
+//     touches fall on distinct banks.
 //   * kPStages LDS stages; loads for stage kt+kPStages-1 are issued right after the barrier of
 //     stage kt; each wave waits (s_waitcnt vmcnt) only for its own loads of the stage it reads.
 //   * Row sub-tiles are dealt to the two wave rows alternately (wave row wm takes 16-row sub-tiles
@@ -19,6 +20,9 @@
 //     into 8 contiguous ranges, one per XCD, walked column-tile fastest, so the workgroups sharing
 //     a block's token rows — and the blocks of one expert sharing weight tiles — run together on
 //     one XCD's L2.
+// Epilogues: gate/up  h = bf16( silu(bf16(g)) * bf16(u) ), g/u dequantised first for FP8
+//            (acc * token scale * output-channel scale); down  Y[slot] = topk_w[slot] * y (FP32),
+//            y = acc (* row scale * output-channel scale for FP8).
 #pragma once
 #include <type_traits>
 
@@ -28,21 +32,17 @@ namespace beam {
 
 constexpr int kPBM = 256;                       // max rows per block
 constexpr int kPBN = 256;                       // weight columns per WG tile
-constexpr int kPBK = 64;                        // K per stage
 constexpr int kPStages = 2;
-constexpr int kPRowBytes = kPBK * 2;            // bytes of one row in one stage
-constexpr int kPChunks = kPBK / 8;              // 16-byte chunks per row per stage
+constexpr int kPRowBytes = 128;                 // bytes of one row in one stage
+constexpr int kPChunks = kPRowBytes / 16;       // 16-byte chunks per row per stage
 constexpr int kPRowsPerLoad = 64 / kPChunks;    // rows covered by one 1 KB wave load
 constexpr int kPLoadsA = kPBM / kPRowsPerLoad;  // wave loads per stage for the token rows
 constexpr int kPLoadsB = kPBN / kPRowsPerLoad;  // ... and for the weight rows
 constexpr int kPLoadsPerWave = (kPLoadsA + kPLoadsB) / 4;
 constexpr int kPStageBytes = (kPBM + kPBN) * kPRowBytes;
-static_assert(kPBK == 32 || kPBK == 64, "swizzle below is defined for 64- and 128-byte rows");
+static_assert(kPChunks == 8, "swizzle below is defined for 128-byte rows");
 static_assert(kPStages >= 2 && kPStageBytes * kPStages <= 160 * 1024, "LDS budget");
 static_assert(kPLoadsPerWave * 3 < 64, "vmcnt range");
-
-// chunk-position swizzle: 8 consecutive rows land their chunk c on 8 distinct 16-byte positions
-__device__ __forceinline__ int pswz(int r) { return kPChunks == 8 ? (r & 7) : ((r >> 1) & 3); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -60,13 +60,45 @@ __device__ __forceinline__ void lds_ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __restrict__ A,
-                                                              const uint16_t* __restrict__ W,
-                                                              const float* __restrict__ topk_w,
-                                                              void* __restrict__ out,
-                                                              AlignTables at, int Kd, int Nout,
-                                                              int topk, int n_ctiles) {
+template <bool FP8>
+struct PipeMath;
+template <>
+struct PipeMath<false> {   // bf16: two 32-deep steps per stage, one 16-byte read per fragment
+  using frag = bf16x8;
+  static constexpr int kSteps = 2, kReads = 1, kElemBytes = 2;
+  __device__ static int chunk(int step, int g, int) { return 4 * step + g; }
+  __device__ static frag read(const unsigned char* p, const int* off) {
+    return *reinterpret_cast<const bf16x8*>(p + off[0]);
+  }
+  __device__ static floatx4 mma(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct PipeMath<true> {    // FP8: one 128-deep step per stage, two 16-byte reads per fragment
+  using frag = intx8;
+  static constexpr int kSteps = 1, kReads = 2, kElemBytes = 1;
+  __device__ static int chunk(int, int g, int half) { return 2 * g + half; }
+  __device__ static frag read(const unsigned char* p, const int* off) {
+    const intx4 lo = *reinterpret_cast<const intx4*>(p + off[0]);
+    const intx4 hi = *reinterpret_cast<const intx4*>(p + off[1]);
+    return frag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  __device__ static floatx4 mma(frag a, frag b, floatx4 c) {
+    // formats 0/0 = E4M3 for both operands; E8M0 block scales 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// A: token rows (gate/up: x, gathered through sorted_slot; down: h in sorted-row order).
+// W: weights [E][rows][Kd]. Kd in elements. a_scale / w_scale: FP8 dequantisation scales
+// (gate/up: per token / per weight row; down: per sorted row / per weight row), unused for bf16.
+template <bool GATE_UP, bool FP8>
+__global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
+    const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
+    const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
+    int topk, int n_ctiles, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
+  using M = PipeMath<FP8>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPStages * kPStageBytes];
   // ---- tile assignment (XCD-aware) ----
   const int L = blockIdx.x;
@@ -81,23 +113,24 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
 
   // ---- direct-load sources. Wave w issues token-row loads a = w*LA .. and weight-row loads
-  // q = w*LB ..; load a covers block rows [a*RPL, (a+1)*RPL): lane -> row a*RPL + lane/CH, chunk
-  // slot lane%CH, global chunk = slot ^ swz(row).
+  // q = w*LB ..; load a covers block rows [8a, 8a+8): lane -> row 8a + lane/8, chunk slot lane%8,
+  // global chunk = slot ^ row%8.
   constexpr int LA = kPLoadsA / 4, LB = kPLoadsB / 4;
   const int lrow = lane / kPChunks;
-  const int gchunk = (lane % kPChunks) ^ pswz(lrow);
-  const uint16_t* asrc[LA];
+  const int gchunk = (lane % kPChunks) ^ lrow;
+  const unsigned char* asrc[LA];
 #pragma unroll
   for (int q = 0; q < LA; ++q) {
     int rr = (wave * LA + q) * kPRowsPerLoad + lrow;   // block row 0..255
     if (rr >= rows) rr = rows - 1;                      // padding rows re-read a valid row
     const int64_t arow =
         GATE_UP ? (int64_t)(at.sorted_slot[row0 + rr] / topk) : (int64_t)(row0 + rr);
-    asrc[q] = A + arow * Kd + gchunk * 8;
+    asrc[q] = A + arow * row_bytes + gchunk * 16;
   }
-  // weight tile row br = (wave*LB + q)*RPL + lrow; gate/up tiles: rows [0,128) gate, [128,256) up.
+  // weight tile row br = (wave*LB + q)*8 + lrow; gate/up tiles: rows [0,128) gate, [128,256) up.
   // A wave's LB loads cover 64 consecutive tile rows, all in one half.
   const int br0 = wave * LB * kPRowsPerLoad + lrow;
   int64_t wrow0;
@@ -105,19 +138,20 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __
     wrow0 = (int64_t)e * 2 * Nout + (br0 < 128 ? 128 * j + br0 : Nout + 128 * j + (br0 - 128));
   else
     wrow0 = (int64_t)e * Nout + 256 * j + br0;
-  const uint16_t* bsrc = W + wrow0 * Kd + gchunk * 8;
-  const int64_t bstep = (int64_t)kPRowsPerLoad * Kd;   // elements between consecutive loads
+  const unsigned char* bsrc = W + wrow0 * row_bytes + gchunk * 16;
+  const int64_t bstep = (int64_t)kPRowsPerLoad * row_bytes;   // bytes between consecutive loads
 
-  auto issue = [&](int stage_k, int buf) {
+  auto issue = [&](int stage, int buf) {
     unsigned char* base = smem + buf * kPStageBytes;
+    const int kb = stage * kPRowBytes;
 #pragma unroll
     for (int q = 0; q < LA; ++q)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[q] + stage_k),
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[q] + kb),
                                        (lds_void_t*)(base + (wave * LA + q) * 1024), 16, 0, 0);
 #pragma unroll
     for (int q = 0; q < LB; ++q)
       __builtin_amdgcn_global_load_lds(
-          (glb_void_t*)(bsrc + q * bstep + stage_k),
+          (glb_void_t*)(bsrc + q * bstep + kb),
           (lds_void_t*)(base + kPBM * kPRowBytes + (wave * LB + q) * 1024), 16, 0, 0);
   };
 
@@ -127,17 +161,20 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = Kd / kPBK;
+  const int nk = (int)(row_bytes / kPRowBytes);
 #pragma unroll
   for (int s = 0; s < kPStages - 1; ++s)
-    if (s < nk) issue(s * kPBK, s);
+    if (s < nk) issue(s, s);
 
-  // fragment byte offset of this lane inside a 16-row group for 32-deep step h of a stage:
-  // row r = lane % 16, chunk 4h + lane/16 (swizzled)
+  // fragment byte offsets of this lane inside a 16-row group, per MFMA step of a stage:
+  // row r = lane % 16, chunk M::chunk(step, lane / 16, half) (swizzled)
   const int r = lane & 15, g = lane >> 4;
-  int frag_off[kPBK / 32];
+  int frag_off[M::kSteps][M::kReads];
 #pragma unroll
-  for (int h = 0; h < kPBK / 32; ++h) frag_off[h] = r * kPRowBytes + (((4 * h + g) ^ pswz(r)) << 4);
+  for (int s = 0; s < M::kSteps; ++s)
+#pragma unroll
+    for (int h = 0; h < M::kReads; ++h)
+      frag_off[s][h] = r * kPRowBytes + ((M::chunk(s, g, h) ^ (r & 7)) << 4);
 
   auto kloop = [&](auto nv_tag) {
     constexpr int NV = decltype(nv_tag)::value;
@@ -149,13 +186,12 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __
         default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPLoadsPerWave)); break;
       }
       lds_ring_barrier();
-      if (kt + kPStages - 1 < nk)
-        issue((kt + kPStages - 1) * kPBK, (kt + kPStages - 1) % kPStages);
+      if (kt + kPStages - 1 < nk) issue(kt + kPStages - 1, (kt + kPStages - 1) % kPStages);
       const unsigned char* sa = smem + (kt % kPStages) * kPStageBytes;
       const unsigned char* sb = sa + kPBM * kPRowBytes;
 #pragma unroll
-      for (int h = 0; h < kPBK / 32; ++h) {
-        bf16x8 bw[8], af[NV];
+      for (int s = 0; s < M::kSteps; ++s) {
+        typename M::frag bw[8], af[NV];
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           int grp;   // 16-row group of the weight tile feeding N sub-tile n of this wave
@@ -163,18 +199,16 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __
             grp = n < 4 ? 4 * wn + n : 8 + 4 * wn + (n - 4);
           else
             grp = 8 * wn + n;
-          bw[n] = *reinterpret_cast<const bf16x8*>(sb + grp * 16 * kPRowBytes + frag_off[h]);
+          bw[n] = M::read(sb + grp * 16 * kPRowBytes, frag_off[s]);
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i)   // 16-row sub-tile wm + 2i of the block
-          af[i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 2 * i) * 16 * kPRowBytes +
-                                                   frag_off[h]);
+          af[i] = M::read(sa + (wm + 2 * i) * 16 * kPRowBytes, frag_off[s]);
         __builtin_amdgcn_sched_barrier(0);   // all reads ahead of the MFMA chain
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
-          for (int n = 0; n < 8; ++n)
-            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[n], acc[i][n], 0, 0, 0);
+          for (int n = 0; n < 8; ++n) acc[i][n] = M::mma(af[i], bw[n], acc[i][n]);
       }
     }
   };
@@ -199,10 +233,17 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __
       const int row = mt * 16 + 4 * g + q;
       if (row >= rows) continue;
       if constexpr (GATE_UP) {
+        float sx = 1.f;
+        if constexpr (FP8) sx = a_scale[at.sorted_slot[row0 + row] / topk];
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const float h = silu_f32(bf16_round(acc[i][n][q])) * bf16_round(acc[i][n + 4][q]);
           const int hcol = 128 * j + 64 * wn + 16 * n + r;
+          float gv = acc[i][n][q], uv = acc[i][n + 4][q];
+          if constexpr (FP8) {
+            gv = gv * sx * w_scale[(int64_t)e * 2 * Nout + hcol];
+            uv = uv * sx * w_scale[(int64_t)e * 2 * Nout + Nout + hcol];
+          }
+          const float h = silu_f32(bf16_round(gv)) * bf16_round(uv);
           reinterpret_cast<uint16_t*>(out)[(int64_t)(row0 + row) * Nout + hcol] =
               (uint16_t)f32_to_bf16_bits(h);
         }
@@ -212,7 +253,9 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(const uint16_t* __
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           const int col = 256 * j + 128 * wn + 16 * n + r;
-          reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = wgt * acc[i][n][q];
+          float y = acc[i][n][q];
+          if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
+          reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = wgt * y;
         }
       }
     }

@@ -1,0 +1,122 @@
+// Weight-streaming grouped GEMM for small row blocks (<= 16 rows; decode-sized batches), gfx950.
+//
+// At decode each touched expert carries a handful of rows, so every weight byte is used once or
+// twice: the kernel is an HBM stream. WG = 4 waves x 16 output columns; each lane streams its
+// weight row(s) straight from HBM into MFMA operand registers (no LDS), 512 bytes of every row per
+// batch with all of a batch's loads issued before its MFMAs. Token rows past the block's rows are
+// zero operands and their results are discarded.
+//   bf16: v_mfma_f32_16x16x32_bf16, lane = row (l % 16), 16 bytes at K slice 8*(l/16) of each
+//         32-deep step; 8 steps per batch.
+//   FP8:  16x16x128 f8f6f4 MFMA (E4M3, unit block scales), 32 bytes at K slice 32*(l/16) of each
+//         128-deep step; 4 steps per batch.
+// Epilogues as in the pipelined kernel: gate/up h = bf16(silu(bf16(g)) * bf16(u)); down
+// Y[slot] = topk_w[slot] * y (FP32); FP8 accumulators are dequantised (token/row scale x output-
+// channel scale) first.
+#pragma once
+#include "common.h"
+
+namespace beam {
+
+constexpr int kSmallBM = 16;
+constexpr int kSmallCols = 64;
+constexpr int kSmallBatchBytes = 512;   // bytes of each operand row per batch
+
+template <bool FP8>
+struct SmallMath;
+template <>
+struct SmallMath<false> {
+  using frag = bf16x8;
+  static constexpr int kStepBytes = 64, kLaneBytes = 16, kElemBytes = 2;
+  __device__ static frag load(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ static frag zero() { return frag{}; }
+  __device__ static floatx4 mma(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct SmallMath<true> {
+  using frag = intx8;
+  static constexpr int kStepBytes = 128, kLaneBytes = 32, kElemBytes = 1;
+  __device__ static frag load(const unsigned char* p) {
+    const intx4 lo = *reinterpret_cast<const intx4*>(p);
+    const intx4 hi = *reinterpret_cast<const intx4*>(p + 16);
+    return frag{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  __device__ static frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0}; }
+  __device__ static floatx4 mma(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+template <bool GATE_UP, bool FP8>
+__global__ __launch_bounds__(256) void grouped_small_kernel(
+    const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
+    const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
+    int topk, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
+  using M = SmallMath<FP8>;
+  constexpr int U = kSmallBatchBytes / M::kStepBytes;   // MFMA steps per batch
+  const int b = blockIdx.y;
+  if (b >= at.n_blocks[0]) return;
+  const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int c0 = blockIdx.x * kSmallCols + wave * 16;
+  const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
+
+  const unsigned char* ap = nullptr;
+  if (r < rows) {
+    if constexpr (GATE_UP)
+      ap = A + (int64_t)(at.sorted_slot[row0 + r] / topk) * row_bytes;
+    else
+      ap = A + (int64_t)(row0 + r) * row_bytes;
+  }
+  const unsigned char* bp0;
+  const unsigned char* bp1 = nullptr;
+  if constexpr (GATE_UP) {
+    bp0 = W + ((int64_t)e * 2 * Nout + c0 + r) * row_bytes;
+    bp1 = W + ((int64_t)e * 2 * Nout + Nout + c0 + r) * row_bytes;
+  } else {
+    bp0 = W + ((int64_t)e * Nout + c0 + r) * row_bytes;
+  }
+  const int koff = g * M::kLaneBytes;
+  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t k = 0; k < row_bytes; k += kSmallBatchBytes) {
+    typename M::frag a[U], w0[U], w1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      w0[u] = M::load(bp0 + k + u * M::kStepBytes + koff);
+      if constexpr (GATE_UP) w1[u] = M::load(bp1 + k + u * M::kStepBytes + koff);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = ap ? M::load(ap + k + u * M::kStepBytes + koff) : M::zero();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc0 = M::mma(a[u], w0[u], acc0);
+      if constexpr (GATE_UP) acc1 = M::mma(a[u], w1[u], acc1);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i;
+    if (row >= rows) continue;
+    const int col = c0 + r;
+    if constexpr (GATE_UP) {
+      float gv = acc0[i], uv = acc1[i];
+      if constexpr (FP8) {
+        const float sx = a_scale[at.sorted_slot[row0 + row] / topk];
+        gv = gv * sx * w_scale[(int64_t)e * 2 * Nout + col];
+        uv = uv * sx * w_scale[(int64_t)e * 2 * Nout + Nout + col];
+      }
+      const float h = silu_f32(bf16_round(gv)) * bf16_round(uv);
+      reinterpret_cast<uint16_t*>(out)[(int64_t)(row0 + row) * Nout + col] =
+          (uint16_t)f32_to_bf16_bits(h);
+    } else {
+      const int slot = at.sorted_slot[row0 + row];
+      float y = acc0[i];
+      if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
+      reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = topk_w[slot] * y;
+    }
+  }
+}
+
+}  // namespace beam

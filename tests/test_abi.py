@@ -130,3 +130,14 @@ def test_valid_call_without_gpu_reports_device():
         pytest.skip("a GPU is present")
     assert _fwd(_cfg()) == DEVICE
     assert _route(_cfg()) == DEVICE
+
+
+def test_quant_fp8_validation():
+    q = bm.lib().beam_moe_quant_fp8
+    assert q(A[0], -1, 5120, A[1], A[2], None) == SHAPE
+    assert q(A[0], 4, 0, A[1], A[2], None) == SHAPE
+    assert q(A[0], 4, 100, A[1], A[2], None) == UNSUP           # cols % 8
+    assert q(A[0], 0, 5120, None, None, None) == OK             # no rows: no-op
+    assert q(None, 4, 5120, A[1], A[2], None) == NULL
+    assert q(A[0] + 2, 4, 5120, A[1], A[2], None) == ALIGN
+    assert q(A[0], 4, 5120, A[0], A[2], None) == ALIAS          # codes on top of the source

@@ -1,0 +1,96 @@
+"""GPU parity of the FP8 E4M3 experts (dynamic per-token / per-row activation scales, per-channel
+weight scales) and of the FP8 quantiser, against the CPU oracle's fp8 contract."""
+import numpy as np
+import pytest
+import torch
+
+import parity
+import routing_grouped_expert_fp32_amd as bm
+import synthgen
+from oracle import codecs, router
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_quant_fp8_bitwise_against_oracle():
+    rng = np.random.default_rng(12)
+    rows = []
+    rows.append(rng.standard_normal(5120) * 3.0)                      # typical activations
+    rows.append(rng.standard_normal(5120) * 1e-3)                     # small values, subnormal codes
+    rows.append(np.zeros(5120))                                       # all-zero row
+    ties = codecs.e4m3_decode(np.arange(0, 0x7E, dtype=np.uint8))     # grid points 0..416
+    mids = (ties[:-1] + ties[1:]) / 2                                 # exact ties when amax = 448
+    r = np.zeros(5120)
+    r[0] = 448.0
+    r[1:1 + len(mids)] = mids
+    r[200:200 + len(mids)] = -mids
+    rows.append(r)
+    z = rng.standard_normal(2560) * 0.25
+    z[7] = -0.0
+    rows.append(np.concatenate([z, z]))
+    for _ in range(27):
+        rows.append(rng.standard_normal(5120) * 10.0 ** rng.uniform(-3, 3))
+    x = torch.tensor(np.stack(rows), dtype=torch.float32).to(torch.bfloat16)
+    codes, scales = bm.quant_fp8(x.cuda())
+    torch.cuda.synchronize()
+    want_c, want_s = codecs.quant_rows_fp8(x.float().numpy())
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, want_c), np.argwhere(got != want_c)[:5]
+    # 2560-wide rows (the h width)
+    c2, s2 = bm.quant_fp8(x[:, :2560].contiguous().cuda())
+    w2c, w2s = codecs.quant_rows_fp8(x[:, :2560].float().numpy())
+    assert np.array_equal(c2.cpu().numpy(), w2c) and np.array_equal(s2.cpu().numpy(), w2s)
+
+
+@pytest.fixture(scope="module")
+def beam_fp8():
+    _say("generating Beam FP8 weights on cuda:0")
+    d = synthgen.make_inputs("fp8_prefill", device="cuda", T=1)
+    torch.cuda.synchronize()
+    return d
+
+
+def _run(name, weights, T=None):
+    wl = synthgen.WORKLOADS[name]
+    d = synthgen.make_inputs(wl, device="cuda", T=T, with_experts=False)
+    T = d["T"]
+    cfg = bm.WorkloadCfg.of(wl.shape, "bf16", "fp8")
+    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    out = bm.forward(d["x"], weights["w_router"], d["bias"], weights["w_gate_up"],
+                     weights["w_down"], cfg, w_gate_up_scale=weights["w_gate_up_scale"],
+                     w_down_scale=weights["w_down_scale"], topk_ids_out=ids)
+    torch.cuda.synchronize()
+    d["w_router"] = weights["w_router"]
+    return wl, d, out, ids
+
+
+@pytest.mark.parametrize("name,T,n_check", [("fp8_decode", None, 32), ("fp8_decode", 77, 77),
+                                            ("fp8_prefill", None, 10), ("fp8_decode", 300, 10)])
+def test_fp8_forward_parity(beam_fp8, name, T, n_check):
+    wl, d, out, ids = _run(name, beam_fp8, T)
+    T = d["T"]
+    _say("fp8 forward", name, "T =", T)
+    sh = wl.shape
+    r = router.route(d["x"].cpu(), d["w_router"].cpu(), d["bias"].cpu(), sh.n_groups,
+                     sh.topk_groups, sh.topk, sh.routed_scale)
+    ids_c = ids.cpu().numpy()
+    rc = parity.check_routing(ids_c, _weights_for(r, ids_c), r)
+    assert not rc["failures"], rc
+    toks = np.arange(T) if T <= n_check else np.sort(np.random.default_rng(T).choice(
+        T, n_check, replace=False))
+    get = parity.expert_loader(beam_fp8["w_gate_up"], beam_fp8["w_down"], sh.d_ff,
+                               beam_fp8["w_gate_up_scale"], beam_fp8["w_down_scale"])
+    err, rms = parity.check_outputs(out.cpu().numpy()[toks], d["x"], ids_c, r, sh.routed_scale,
+                                    get, "fp8", toks)
+    _say(name, T, "fp8 max|err|/rms", err)
+    assert err <= parity.TOL["fp8"]
+
+
+def _weights_for(r, ids_c):
+    """Oracle weights in the GPU's id order (the routing check compares per expert id)."""
+    return router.weights(r.s, ids_c.astype(np.int64), 2.5)
