@@ -1,24 +1,25 @@
 """Benchmark of the Beam routed-MoE block on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skew]
-                    [--also prefill] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+                    [--also prefill,fp8_decode,fp8_prefill] [--no-cpu-baseline]
 
-A step is one beam_moe_forward over one batch (router, selection, moe_align, gate/up GEMM, down
-GEMM, combine), inputs already resident in HBM. The timed region is bracketed by
-torch.cuda.synchronize() on both sides; per-stage HIP events recorded by the library on the
-call's stream during the same timed steps give each kernel's average duration. Prints ONE JSON
-line.
+A step is one beam_moe_forward over one batch (router, selection, moe_align, [FP8 quantisers],
+gate/up GEMM, down GEMM, combine), inputs already resident in HBM. The timed region is bracketed by
+torch.cuda.synchronize() on both sides; per-stage HIP events recorded by the library on the call's
+stream during the same timed steps give each kernel's average duration. Prints ONE JSON line; the
+headline `value` is the --workload (decode, T=32, the configuration the metric is quoted on), the
+other workloads are reported under "also".
 
-roofline (dominant kernel = the gate/up grouped GEMM): algorithmic bytes per launch =
-  distinct experts touched (counted from the routing of the batch) * 2 * d_ff * hidden * 2 B
-  (the gate and up weights, read once) + T * hidden * 2 B (x, read once) + T * K * d_ff * 2 B
-(h written once), divided by the kernel's average duration. Each weight byte (bf16) feeds one
-multiply-add per routed row, so the kernel's FLOP per weight byte equals the rows per expert
-T*K/E: below the bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312) the bound is "hbm", else "mfma" with
-algorithmic FLOP = 2 * T * K * 2 * d_ff * hidden.
-traffic: FETCH_SIZE + WRITE_SIZE of the kernel from rocprofv3 --pmc runs recorded in
-profiles/counters_<workload>.json, scaled by the same counters on a plain copy; null if that file
-is missing or was taken on a different version of the kernel source.
+roofline (dominant kernel = the gate/up grouped GEMM). Algorithmic bytes per launch = distinct
+experts touched (counted from the routing of the batch) x the expert's gate and up weights (bf16:
+2*d_ff*hidden*2 B; FP8: 2*d_ff*hidden codes + 2*d_ff*4 B scales) + the token rows read once (bf16 x,
+or FP8 codes + scales) + h written once (T*K*d_ff*2 B), divided by the kernel's average duration.
+Each weight byte feeds one multiply-add per routed row (bf16: 2 FLOP / 2 B; FP8: 2 FLOP / 1 B), so
+FLOP/B = T*K/E (bf16) or 2*T*K/E (FP8); below the ridge (bf16 2.5 PFLOP/s / 8 TB/s = 312; FP8
+5.0 / 8 = 625) the bound is "hbm", else "mfma" with FLOP = 2*T*K*2*d_ff*hidden.
+traffic: HBM bytes of that kernel from rocprofv3 --pmc runs (2.0 x FETCH_SIZE + WRITE_SIZE, the
+factor from a 1 GiB copy), stored in profiles/counters_<workload>.json with a hash of the kernel
+sources; null if the file is missing or the sources changed since.
 cpu_baseline: the CPU oracle (float64 numpy) on a bounded sample of the same batch (routing of the
 whole batch + expert MLPs and combine for the first --cpu-tokens tokens), on the host's cores.
 """
@@ -35,13 +36,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
-FP8_PEAK_TFLOPS = 5000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+KERNEL_SOURCES = ("gemm_grouped.hip", "gemm_pipe.h", "gemm_small.h", "common.h")
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm_bf16.hip", "common.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "routing_grouped_expert_fp32_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -52,10 +53,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew"])
-    p.add_argument("--also", default="prefill", help="comma list of extra workloads ('' = none)")
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill"])
+    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill",
+                   help="comma list of extra workloads ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=4)
+    p.add_argument("--cpu-tokens", type=int, default=32)
     p.add_argument("--copy-probe-gib", type=float, default=0.0,
                    help="also run a plain device copy of this size (counter scaling reference)")
     return p.parse_args()
@@ -66,21 +69,39 @@ def skew_delta():
         return json.load(f)["delta"]
 
 
+class Weights:
+    """Beam expert weights on the GPU, generated once per dtype."""
+
+    def __init__(self, synthgen, torch):
+        self.sg, self.torch, self.cache = synthgen, torch, {}
+
+    def get(self, w_dtype):
+        if w_dtype not in self.cache:
+            name = "fp8_prefill" if w_dtype == "fp8" else "prefill"
+            print(f"[bench] generating Beam {w_dtype} expert weights", file=sys.stderr, flush=True)
+            self.cache[w_dtype] = self.sg.make_inputs(name, device="cuda", T=1)
+            self.torch.cuda.synchronize()
+        return self.cache[w_dtype]
+
+
 def measure(bm, synthgen, torch, name, weights, steps, warmup):
     wl = synthgen.WORKLOADS[name]
+    W = weights.get(wl.w_dtype)
     d = synthgen.make_inputs(wl, device="cuda", with_experts=False,
                              skew_delta=skew_delta() if name == "skew" else None)
     sh = wl.shape
+    fp8 = wl.w_dtype == "fp8"
     cfg = bm.WorkloadCfg.of(sh, wl.x_dtype, wl.w_dtype)
     T = wl.T
     ws = torch.empty(bm.workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda")
     ids = torch.empty((T, sh.topk), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    scales = dict(w_gate_up_scale=W.get("w_gate_up_scale"), w_down_scale=W.get("w_down_scale"))
 
     def step():
-        bm.forward(d["x"], weights["w_router"], d["bias"], weights["w_gate_up"],
-                   weights["w_down"], cfg, out=out, topk_ids_out=ids, workspace=ws, stream=stream)
+        bm.forward(d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg, out=out,
+                   topk_ids_out=ids, workspace=ws, stream=stream, **scales)
 
     for _ in range(warmup):
         step()
@@ -95,25 +116,32 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
     bm.timing_enable(False)
     stages = bm.timing_collect()
     distinct = int(torch.unique(ids).numel())
-    F, H, K = sh.d_ff, sh.hidden, sh.topk
+    F, H, K, E = sh.d_ff, sh.hidden, sh.topk, sh.n_experts
+    wb = 1 if fp8 else 2                                   # bytes per weight element
+    gu_w = 2 * F * H * wb + (2 * F * 4 if fp8 else 0)      # gate+up bytes of one expert
+    dn_w = H * F * wb + (H * 4 if fp8 else 0)
+    x_bytes = T * H * (1 + 4.0 / H if fp8 else 2)
     gu_ms = stages["gate_up"][0] / max(stages["gate_up"][1], 1)
-    gu_bytes = distinct * 2 * F * H * 2 + T * H * 2 + T * K * F * 2
+    gu_bytes = distinct * gu_w + x_bytes + T * K * F * 2
     gu_flops = 2.0 * T * K * 2 * F * H
-    rows_per_expert = T * K / sh.n_experts
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    layer_bytes = distinct * 3 * F * H * 2 + sh.n_experts * H * 4 + sh.n_experts * 4 + T * H * 2 \
-        + T * H * 4
+    flop_per_byte = (2.0 if fp8 else 1.0) * T * K / E
+    dt = "fp8" if fp8 else "bf16"
+    ridge = PEAK_TFLOPS[dt] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    layer_bytes = distinct * (gu_w + dn_w) + E * H * 4 + E * 4 + T * H * 2 + T * H * 4
     layer_flops = 2.0 * T * K * 3 * F * H
     ms = elapsed * 1e3 / steps
     res = {
-        "workload": name, "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
-        "layer_TBps": layer_bytes / (ms * 1e-3) / 1e12, "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
+        "workload": name, "T": T, "dtype": dt, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+        "layer_TBps": layer_bytes / (ms * 1e-3) / 1e12,
+        "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
+        "layer_frac_of_mfma_peak": layer_flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[dt],
         "distinct_experts": distinct,
         "stages_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items()},
         "gate_up": {"ms": gu_ms, "bytes": gu_bytes, "flops": gu_flops,
                     "GBps": gu_bytes / (gu_ms * 1e-3) / 1e9,
                     "TFLOPs": gu_flops / (gu_ms * 1e-3) / 1e12},
-        "bound": "hbm" if rows_per_expert < ridge else "mfma",
+        "bound": "hbm" if flop_per_byte < ridge else "mfma",
+        "small_blocks": T * K <= 4 * E,
     }
     del ws, out
     return res, d, ids
@@ -125,10 +153,11 @@ def roofline(r, workload):
         roof = {"bound": "hbm", "achieved": g["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": g["GBps"] / HBM_PEAK_GBS}
     else:
-        roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": g["TFLOPs"] / BF16_PEAK_TFLOPS}
-    roof["kernel"] = "gate_up (grouped_%s_kernel<true>)" % ("small" if r["T"] * 8 <= 1024 else
-                                                            "tiled")
+        pk = PEAK_TFLOPS[r["dtype"]]
+        roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": pk, "unit": "TFLOP/s",
+                "frac": g["TFLOPs"] / pk}
+    kind = "small" if r["small_blocks"] else "pipe"
+    roof["kernel"] = f"gate_up: grouped_{kind}_kernel<true, {str(r['dtype'] == 'fp8').lower()}>"
     roof["algorithmic_bytes_per_launch"] = g["bytes"]
     roof["traffic"] = None
     cpath = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
@@ -140,18 +169,18 @@ def roofline(r, workload):
     return roof
 
 
-def cpu_baseline(torch, synthgen, d, weights, ids_gpu, wl_name, n_tok):
+def cpu_baseline(torch, synthgen, d, W, wl_name, n_tok):
     """The oracle as it stands, on the host cores: full-batch routing plus the expert MLPs and
     combine of the first n_tok tokens (their experts' weights copied to the host beforehand)."""
-    import numpy as np
     from oracle import experts, router
     wl = synthgen.WORKLOADS[wl_name]
     sh = wl.shape
-    x_h, wr_h, b_h = d["x"].cpu(), weights["w_router"].cpu(), d["bias"].cpu()
+    x_h, wr_h, b_h = d["x"].cpu(), W["w_router"].cpu(), d["bias"].cpu()
     toks = list(range(n_tok))
-    r0 = router.route(x_h[:n_tok], wr_h, b_h, sh.n_groups, sh.topk_groups, sh.topk, sh.routed_scale)
+    r0 = router.route(x_h[:n_tok], wr_h, b_h, sh.n_groups, sh.topk_groups, sh.topk,
+                      sh.routed_scale)
     need = sorted(set(int(e) for e in r0.ids.ravel()))
-    host_w = {e: (weights["w_gate_up"][e].cpu(), weights["w_down"][e].cpu()) for e in need}
+    host_w = {e: (W["w_gate_up"][e].cpu(), W["w_down"][e].cpu()) for e in need}
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -166,9 +195,8 @@ def cpu_baseline(torch, synthgen, d, weights, ids_gpu, wl_name, n_tok):
     t_exp = time.perf_counter() - t1
     # per-token cost of the whole block: routing amortised over the batch + experts per token
     per_tok = t_route / wl.T + t_exp / n_tok
-    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": int(max(blas,
-                                                                          torch.get_num_threads())),
-            "kind": "oracle",
+    return {"value": 1.0 / per_tok, "unit": "tokens/s",
+            "cores": int(max(blas, torch.get_num_threads())), "kind": "oracle",
             "sample": f"{wl_name}: routing of all {wl.T} tokens ({t_route:.2f} s) + expert MLPs and "
                       f"combine of {n_tok} tokens / {n_tok * sh.topk} expert calls ({t_exp:.2f} s), "
                       f"float64 numpy"}
@@ -185,10 +213,8 @@ def main():
     import synthgen
     bm.lib()
     torch.cuda.set_device(0)
-    print(f"[bench] generating Beam bf16 weights on {torch.cuda.get_device_name(0)}",
-          file=sys.stderr, flush=True)
-    weights = synthgen.make_inputs("prefill", device="cuda", T=1)
-    torch.cuda.synchronize()
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    weights = Weights(synthgen, torch)
     main_res, d, ids = measure(bm, synthgen, torch, a.workload, weights, a.steps, a.warmup)
     print(f"[bench] {a.workload}: {main_res['ms_per_step']:.3f} ms/step", file=sys.stderr,
           flush=True)
@@ -206,20 +232,20 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     cpu = None
+    wl = synthgen.WORKLOADS[a.workload]
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(torch, synthgen, d, weights, ids, a.workload, a.cpu_tokens)
-    wl = synthgen.WORKLOADS[a.workload]
+        cpu = cpu_baseline(torch, synthgen, d, weights.get(wl.w_dtype), a.workload, a.cpu_tokens)
     sh = wl.shape
     line = {
         "metric": "MoE-layer tokens/sec (d5120, 256 exp, top-8); % of roofline",
         "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": main_res["dtype"], "data": "synthetic",
         "config": {"workload": f"{a.workload}: Beam MoE layer, T={wl.T}, hidden {sh.hidden}, "
                                f"{sh.n_experts} experts ({sh.n_groups} groups, keep "
-                               f"{sh.topk_groups}), top-{sh.topk}, d_ff {sh.d_ff}, bf16 experts, "
-                               f"FP32 router, fp32 out",
+                               f"{sh.topk_groups}), top-{sh.topk}, d_ff {sh.d_ff}, "
+                               f"{main_res['dtype']} experts, FP32 router, fp32 out",
                    "T": wl.T, "global_batch": wl.T, "parallelism": "single GPU"},
         "roofline": roofline(main_res, a.workload),
         "cpu_baseline": cpu,
