@@ -11,8 +11,10 @@
 //     lines) contiguously in LDS; each lane fetches the 16-byte chunk that belongs at its LDS slot.
 //     Chunk c of row r is stored at chunk position c ^ (r & 7), so the 16 rows a fragment read
 //     touches fall on distinct banks.
-//   * kPStages LDS stages; loads for stage kt+kPStages-1 are issued right after the barrier of
-//     stage kt; each wave waits (s_waitcnt vmcnt) only for its own loads of the stage it reads.
+//   * Separate LDS rings: token rows (L2-resident, short latency) 2 stages, issued one stage
+//     ahead; weights (streamed from HBM) 3 stages, issued two stages ahead, so more weight bytes
+//     are in flight (2 x 32 KB per CU); 160 KB in all. Each wave waits (s_waitcnt vmcnt) only for
+//     its own loads of the stage it reads.
 //   * Row sub-tiles are dealt to the two wave rows alternately (wave row wm takes 16-row sub-tiles
 //     wm, wm+2, ...); a wave runs one of four K-loop bodies (2, 4, 6 or 8 sub-tiles), chosen by how
 //     many of its sub-tiles hold rows, so a partly filled block costs about its rows.
@@ -32,17 +34,24 @@ namespace beam {
 
 constexpr int kPBM = 256;                       // max rows per block
 constexpr int kPBN = 256;                       // weight columns per WG tile
-constexpr int kPStages = 2;
+constexpr int kPAStages = 2;                    // token-row ring depth
+constexpr int kPBStages = 3;                    // weight ring depth
 constexpr int kPRowBytes = 128;                 // bytes of one row in one stage
 constexpr int kPChunks = kPRowBytes / 16;       // 16-byte chunks per row per stage
 constexpr int kPRowsPerLoad = 64 / kPChunks;    // rows covered by one 1 KB wave load
 constexpr int kPLoadsA = kPBM / kPRowsPerLoad;  // wave loads per stage for the token rows
 constexpr int kPLoadsB = kPBN / kPRowsPerLoad;  // ... and for the weight rows
 constexpr int kPLoadsPerWave = (kPLoadsA + kPLoadsB) / 4;
-constexpr int kPStageBytes = (kPBM + kPBN) * kPRowBytes;
+constexpr int kPAStageBytes = kPBM * kPRowBytes;
+constexpr int kPBStageBytes = kPBN * kPRowBytes;
+constexpr int kPLdsBytes = kPAStages * kPAStageBytes + kPBStages * kPBStageBytes;
 static_assert(kPChunks == 8, "swizzle below is defined for 128-byte rows");
-static_assert(kPStages >= 2 && kPStageBytes * kPStages <= 160 * 1024, "LDS budget");
+static_assert(kPLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kPLoadsPerWave * 3 < 64, "vmcnt range");
+
+// cache-policy operand of the direct loads: non-temporal for the weight stream (each weight byte
+// is read by one workgroup pair, so it should not push the shared token rows out of L2)
+constexpr int kCachePolicyNT = 2;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -99,7 +108,9 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
     const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, int n_ctiles, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
   using M = PipeMath<FP8>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kPStages * kPStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPLdsBytes];
+  unsigned char* const aring = smem;
+  unsigned char* const bring = smem + kPAStages * kPAStageBytes;
   // ---- tile assignment (XCD-aware) ----
   const int L = blockIdx.x;
   const int xcd = L & 7, local = L >> 3;
@@ -141,18 +152,22 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
   const unsigned char* bsrc = W + wrow0 * row_bytes + gchunk * 16;
   const int64_t bstep = (int64_t)kPRowsPerLoad * row_bytes;   // bytes between consecutive loads
 
-  auto issue = [&](int stage, int buf) {
-    unsigned char* base = smem + buf * kPStageBytes;
+  auto issue_a = [&](int stage) {
+    unsigned char* base = aring + (stage % kPAStages) * kPAStageBytes;
     const int kb = stage * kPRowBytes;
 #pragma unroll
     for (int q = 0; q < LA; ++q)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[q] + kb),
                                        (lds_void_t*)(base + (wave * LA + q) * 1024), 16, 0, 0);
+  };
+  auto issue_b = [&](int stage) {
+    unsigned char* base = bring + (stage % kPBStages) * kPBStageBytes;
+    const int kb = stage * kPRowBytes;
 #pragma unroll
     for (int q = 0; q < LB; ++q)
-      __builtin_amdgcn_global_load_lds(
-          (glb_void_t*)(bsrc + q * bstep + kb),
-          (lds_void_t*)(base + kPBM * kPRowBytes + (wave * LB + q) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(bsrc + q * bstep + kb),
+                                       (lds_void_t*)(base + (wave * LB + q) * 1024), 16, 0,
+                                       kCachePolicyNT);
   };
 
   floatx4 acc[8][8];
@@ -161,10 +176,13 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Issue order: prologue A(0), B(0), B(1); iteration kt issues A(kt+1), B(kt+2). Entering
+  // iteration kt the wave's queue ends with B(kt), A(kt), B(kt+1): all but the youngest LB loads
+  // must have completed.
   const int nk = (int)(row_bytes / kPRowBytes);
-#pragma unroll
-  for (int s = 0; s < kPStages - 1; ++s)
-    if (s < nk) issue(s, s);
+  issue_a(0);
+  issue_b(0);
+  if (1 < nk) issue_b(1);
 
   // fragment byte offsets of this lane inside a 16-row group, per MFMA step of a stage:
   // row r = lane % 16, chunk M::chunk(step, lane / 16, half) (swizzled)
@@ -179,16 +197,15 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
   auto kloop = [&](auto nv_tag) {
     constexpr int NV = decltype(nv_tag)::value;
     for (int kt = 0; kt < nk; ++kt) {
-      const int younger = min(kPStages - 2, nk - 1 - kt);   // stages issued after this one
-      switch (younger) {
-        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPLoadsPerWave)); break;
-        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPLoadsPerWave)); break;
-      }
+      if (kt + 1 < nk)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LB));   // B(kt+1) may stay in flight
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_ring_barrier();
-      if (kt + kPStages - 1 < nk) issue(kt + kPStages - 1, (kt + kPStages - 1) % kPStages);
-      const unsigned char* sa = smem + (kt % kPStages) * kPStageBytes;
-      const unsigned char* sb = sa + kPBM * kPRowBytes;
+      if (kt + 1 < nk) issue_a(kt + 1);
+      if (kt + 2 < nk) issue_b(kt + 2);
+      const unsigned char* sa = aring + (kt % kPAStages) * kPAStageBytes;
+      const unsigned char* sb = bring + (kt % kPBStages) * kPBStageBytes;
 #pragma unroll
       for (int s = 0; s < M::kSteps; ++s) {
         typename M::frag bw[8], af[NV];
