@@ -173,12 +173,20 @@ struct StageTimer {
       a = b = nullptr;
       return;
     }
-    hipEventRecord(a, st);
+    if (hipEventRecord(a, st) != hipSuccess) release();
   }
   ~StageTimer() {
     if (!a) return;
-    hipEventRecord(b, st);
+    if (hipEventRecord(b, st) != hipSuccess) {
+      release();
+      return;
+    }
     g_recs.push_back({stage, a, b});
+  }
+  void release() {   // a failed record: drop this stage's events (timing is best effort)
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    a = b = nullptr;
   }
 };
 
@@ -385,8 +393,8 @@ int32_t beam_moe_timing_collect(double* total_ms, int32_t* launches, int32_t n_s
       if (total_ms) total_ms[r.stage] += ms;
       if (launches) launches[r.stage] += 1;
     }
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_recs.clear();
   return kNumStages;

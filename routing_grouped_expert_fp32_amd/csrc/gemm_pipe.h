@@ -49,8 +49,8 @@ static_assert(kPChunks == 8, "swizzle below is defined for 128-byte rows");
 static_assert(kPLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kPLoadsPerWave * 3 < 64, "vmcnt range");
 
-// cache-policy operand of the direct loads: non-temporal for the weight stream (each weight byte
-// is read by one workgroup pair, so it should not push the shared token rows out of L2)
+// cache-policy operand of the direct loads: non-temporal for the weight stream (a weight tile is
+// read once per row block of its expert, so it should not push the shared token rows out of L2)
 constexpr int kCachePolicyNT = 2;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
