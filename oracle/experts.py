@@ -92,6 +92,34 @@ def forward_expert_major(x, ids, w, get_expert: Callable[[int], dict], contract:
     return (out, contrib) if return_contrib else out
 
 
+def forward_routed(x, ids, w, get_expert: Callable[[int], dict], contract: str,
+                   expert_begin: int = 0, expert_end: int | None = None):
+    """Routed MoE output from given routes, restricted to the experts [expert_begin, expert_end).
+
+    Replayed routes are used as recorded instead of being recomputed ([S] §Reinforcement learning
+    in Miles); an expert-parallel rank gets explicit ids and weights and computes only its own
+    experts ([S] §Fusion Optimizations). Reading: a slot whose expert lies outside the range
+    contributes nothing; the remaining contributions w * y are added in k order, starting from 0.
+    get_expert(e) takes the global expert id.
+    """
+    x = to_f64(x)
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float64)
+    T, K = ids.shape
+    hi = np.inf if expert_end is None else expert_end   # None: no upper bound
+    out = np.zeros((T, x.shape[1]), dtype=np.float64)
+    contrib = np.zeros((T, K, x.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        if not expert_begin <= e < hi:
+            continue
+        t_idx, k_idx = np.nonzero(ids == e)
+        y = expert_mlp(x[t_idx], get_expert(int(e)), contract)
+        contrib[t_idx, k_idx, :] = w[t_idx, k_idx][:, None] * y
+    for k in range(K):
+        out = out + contrib[:, k, :]
+    return out
+
+
 def forward_token_major(x, ids, w, get_expert: Callable[[int], dict], contract: str):
     """Same result as forward_expert_major, computed one token and one expert at a time."""
     x = to_f64(x)

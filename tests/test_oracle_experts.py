@@ -171,3 +171,43 @@ def test_fp8_contract_exact_case():
         for n in range(H8):
             want = ex["down_scale"][n] * sum(down_codes[n, f] * hd[f] for f in range(F8))
             assert abs(y[t][n] - want) <= 1e-14 * max(1.0, abs(want))
+
+
+def test_routed_range_closed_form():
+    """Given routes over a range of experts ([S] §Fusion Optimizations, §Reinforcement learning in
+    Miles): only slots routed into [begin, end) contribute, with their weights as given; ids
+    outside [0, E) never contribute."""
+    rng = np.random.default_rng(11)
+    c = [0.5, -1.25, 2.0, 0.75]
+    ex = _selector_experts(c)
+    T, K = 7, 3
+    x = rng.standard_normal((T, H))
+    x[:, 0] = 1.0
+    ids = np.array([[0, 1, 2], [3, 2, 1], [1, 3, 0], [2, 0, 3], [0, 3, -1], [1, 2, 9], [3, 0, 1]])
+    w = rng.uniform(-1.0, 2.0, size=(T, K))   # arbitrary: no renormalisation is implied
+    for begin, end in [(0, 4), (1, 3), (2, 3), (0, 1), (3, 4), (2, 2)]:
+        out = experts.forward_routed(x, ids, w, lambda e: ex[e], "fp32", begin, end)
+        for t in range(T):
+            for n in range(H):
+                want = sum(w[t][k] * (ids[t][k] + 1) * c[ids[t][k]] * _silu(x[t][1 + _perm(n)])
+                           for k in range(K) if begin <= ids[t][k] < end)
+                assert abs(out[t][n] - want) <= 1e-14 * max(1.0, abs(want)), (begin, end, t, n)
+
+
+@pytest.mark.parametrize("contract", ["fp32", "bf16"])
+def test_routed_partition_sums_to_forward(contract):
+    """Outputs over a partition of the experts add up to the full routed MoE output; the full range
+    reproduces it exactly."""
+    rng = np.random.default_rng(12)
+    ex = {e: {"gate": rng.standard_normal((F, H)) * 0.3, "up": rng.standard_normal((F, H)) * 0.3,
+              "down": rng.standard_normal((H, F)) * 0.3} for e in range(E)}
+    T, K = 9, 2
+    x = rng.standard_normal((T, H))
+    ids = np.array([rng.choice(E, size=K, replace=False) for _ in range(T)])
+    w = rng.uniform(0.1, 1.5, size=(T, K))
+    full = experts.forward_expert_major(x, ids, w, lambda e: ex[e], contract)
+    np.testing.assert_array_equal(
+        experts.forward_routed(x, ids, w, lambda e: ex[e], contract, 0, E), full)
+    parts = sum(experts.forward_routed(x, ids, w, lambda e: ex[e], contract, b, e)
+                for b, e in [(0, 1), (1, 3), (3, 4)])
+    np.testing.assert_allclose(parts, full, rtol=1e-12, atol=1e-12)
