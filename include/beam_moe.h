@@ -129,6 +129,38 @@ BEAM_API beam_status_t beam_moe_forward(const void* x, const float* w_router, co
                                void* stream);
 BEAM_API size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int64_t T);
 
+/* Steps 4-5 with given routes, over a range of experts (routing replay and the expert-parallel
+ * entry point: the routes are recorded once and reused instead of recomputed, so near-tied router
+ * scores cannot pick a different expert path, [S] §Reinforcement learning in Miles; an expert-
+ * parallel rank receives explicit expert ids and routing weights and runs its own experts,
+ * including ranks with no local tokens, [S] §Fusion Optimizations).
+ *   x          [T][H] x_dtype (as for beam_moe_forward)
+ *   topk_ids   [T][K] int32: expert ids of each token's slots, as beam_moe_route writes them. Ids
+ *              outside [expert_begin, expert_end) (including ids outside [0, E)) are skipped. Ids of
+ *              one token must be distinct; a repeated id gives that token an unspecified (but
+ *              memory-safe) output.
+ *   topk_w     [T][K] fp32 routing weights, used as given (no renormalisation, no routed_scale)
+ *   expert_begin, expert_end  the local experts, 0 <= expert_begin <= expert_end <= E
+ *   w_gate_up  [expert_end - expert_begin][2F][H] w_dtype: the local experts' weights, local expert
+ *              i being expert expert_begin + i (layout per expert as for beam_moe_forward)
+ *   w_down     [expert_end - expert_begin][H][F] w_dtype
+ *   w_gate_up_scale [expert_end - expert_begin][2F], w_down_scale [expert_end - expert_begin][H]:
+ *              FP8 only, as for beam_moe_forward (NULL otherwise)
+ *   With an empty range (expert_begin == expert_end) the weight and scale pointers may be NULL.
+ *   out        [T][H] out_dtype: out[t] = sum, in k order from +0, over the slots k whose id e lies in
+ *              the range, of topk_w[t][k] * expert_e(x[t]). Tokens without such slots get zeros. With
+ *              the full range [0, E) and the routes of beam_moe_route this equals beam_moe_forward;
+ *              summing the outputs of a partition of [0, E) gives it up to FP32 reassociation.
+ *   workspace  device scratch of at least beam_moe_workspace_bytes(cfg, T) bytes
+ * Validation and errors as for beam_moe_forward; a bad range is BEAM_ERR_SHAPE. */
+BEAM_API beam_status_t beam_moe_forward_routed(const void* x, const int32_t* topk_ids,
+                                               const float* topk_w, const void* w_gate_up,
+                                               const void* w_down, void* out, int64_t T,
+                                               const beam_moe_cfg* cfg, int32_t expert_begin,
+                                               int32_t expert_end, const float* w_gate_up_scale,
+                                               const float* w_down_scale, void* workspace,
+                                               size_t workspace_bytes, void* stream);
+
 /* Dynamic FP8 E4M3 quantisation of bf16 rows, the activation step of the FP8 experts (dynamic FP8
  * checkpoints: [S] §Highlights, §BF16, NVFP4 and FP8 Model Support).
  *   src    [rows][cols] bf16 (device), cols % 8 == 0

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "BEAM_F32", "BEAM_BF16", "BEAM_FP8_E4M3", "Cfg", "make_cfg", "lib", "lib_path", "route",
     "forward", "workspace_bytes", "route_workspace_bytes", "BeamError", "timing_enable",
-    "timing_collect", "STAGES", "status_string", "quant_fp8",
+    "timing_collect", "STAGES", "status_string", "quant_fp8", "forward_routed",
 ]
 
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_timing_collect.restype = i32
         L.beam_moe_stage_name.argtypes = [i32]
         L.beam_moe_stage_name.restype = ctypes.c_char_p
+        L.beam_moe_forward_routed.argtypes = [vp, vp, vp, vp, vp, vp, i64, cfgp, i32, i32, vp,
+                                              vp, vp, sz, vp]
+        L.beam_moe_forward_routed.restype = i32
         L.beam_moe_quant_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
         L.beam_moe_quant_fp8.restype = i32
         _LIB = L
@@ -163,6 +166,32 @@ def forward(x, w_router, bias, w_gate_up, w_down, cfg: Cfg, out=None, w_gate_up_
                                 _stream(stream))
     if rc != 0:
         raise BeamError(rc, "beam_moe_forward")
+    return out
+
+
+def forward_routed(x, topk_ids, topk_w, w_gate_up, w_down, cfg: Cfg, expert_begin: int = 0,
+                   expert_end: int | None = None, out=None, w_gate_up_scale=None,
+                   w_down_scale=None, workspace=None, stream=None):
+    """beam_moe_forward_routed: out [T][H] from given routes over experts [expert_begin,
+    expert_end); w_gate_up / w_down (and the FP8 scales) hold only those experts."""
+    T = x.shape[0]
+    if expert_end is None:
+        expert_end = cfg.n_experts
+    if out is None:
+        odt = torch.bfloat16 if cfg.out_dtype == BEAM_BF16 else torch.float32
+        out = torch.empty((T, cfg.hidden), dtype=odt, device=x.device)
+    nbytes = workspace_bytes(cfg, T)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check_dev(x, topk_ids, topk_w, w_gate_up, w_down, out, w_gate_up_scale, w_down_scale,
+               workspace)
+    rc = lib().beam_moe_forward_routed(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gate_up),
+                                       _ptr(w_down), _ptr(out), T, ctypes.byref(cfg),
+                                       int(expert_begin), int(expert_end), _ptr(w_gate_up_scale),
+                                       _ptr(w_down_scale), _ptr(workspace), workspace.numel(),
+                                       _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_forward_routed")
     return out
 
 

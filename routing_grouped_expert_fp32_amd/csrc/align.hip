@@ -14,7 +14,11 @@
 //                    earlier tokens of the chunk that chose the same expert (popcount of the mask
 //                    below the token's bit). Rows of an expert are therefore in token order — a
 //                    deterministic, stable permutation; no sort, no global atomics.
-// Slots of one token name distinct experts (the router guarantees it).
+// Only the experts [e_begin, e_begin + E) take part (the forward uses all of them; a routed call
+// may restrict itself to a local range): slots naming any other id are left out, and expert
+// indices in the tables are local (id - e_begin), so the GEMMs index a local weight array.
+// Slots of one token name distinct experts (the router guarantees it; for given routes a repeated
+// id within a token leaves one of its slots out, which is memory-safe).
 #include "common.h"
 
 namespace beam {
@@ -25,7 +29,7 @@ constexpr int kWords = kAlignWords;
 __global__ __launch_bounds__(256) void align_count_kernel(const int32_t* __restrict__ ids,
                                                           uint64_t* __restrict__ chunk_mask,
                                                           int32_t* __restrict__ chunk_cnt,
-                                                          int64_t T, int E, int K) {
+                                                          int64_t T, int E, int K, int e_begin) {
   __shared__ unsigned long long mask[256 * kWords];
   const int c = blockIdx.x;
   for (int i = threadIdx.x; i < E * kWords; i += 256) mask[i] = 0ull;
@@ -35,7 +39,8 @@ __global__ __launch_bounds__(256) void align_count_kernel(const int32_t* __restr
   const int nslot = ntok * K;
   for (int i = threadIdx.x; i < nslot; i += 256) {
     const int tl = i / K;
-    const int e = ids[tbeg * K + i];
+    const int e = ids[tbeg * K + i] - e_begin;
+    if ((unsigned)e >= (unsigned)E) continue;   // not one of this call's experts
     atomicOr(&mask[e * kWords + (tl >> 6)], 1ull << (tl & 63));
   }
   __syncthreads();
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
                                                             const int32_t* __restrict__ chunk_base,
                                                             const int32_t* __restrict__ expert_off,
                                                             int32_t* __restrict__ sorted_slot,
-                                                            int64_t T, int E, int K) {
+                                                            int64_t T, int E, int K, int e_begin) {
   __shared__ unsigned long long mask[256 * kWords];
   __shared__ int base[256];
   const int c = blockIdx.x;
@@ -161,7 +166,8 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   const int nslot = ntok * K;
   for (int i = threadIdx.x; i < nslot; i += 256) {
     const int tl = i / K;
-    const int e = ids[tbeg * K + i];
+    const int e = ids[tbeg * K + i] - e_begin;
+    if ((unsigned)e >= (unsigned)E) continue;
     const int w = tl >> 6;
     int rank = 0;
     for (int q = 0; q < w; ++q) rank += __popcll(mask[e * kWords + q]);
@@ -172,20 +178,20 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
 }
 
 hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
-                        hipStream_t st) {
+                        int e_begin, int e_count, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const int n_chunks = (int)ceil_div(s.T, kChunk);
   hipLaunchKernelGGL(align_count_kernel, dim3(n_chunks), dim3(256), 0, st, ids, at.chunk_mask,
-                     at.chunk_base, s.T, s.E, s.K);
+                     at.chunk_base, s.T, e_count, s.K, e_begin);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, st, at.chunk_base,
                      at.expert_count, at.expert_off, at.n_blocks, at.blk_expert, at.blk_row0,
-                     at.blk_rows, n_chunks, s.E, BM);
+                     at.blk_rows, n_chunks, e_count, BM);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(align_scatter_kernel, dim3(n_chunks), dim3(256), 0, st, ids, at.chunk_mask,
-                     at.chunk_base, at.expert_off, at.sorted_slot, s.T, s.E, s.K);
+                     at.chunk_base, at.expert_off, at.sorted_slot, s.T, e_count, s.K, e_begin);
   return hipGetLastError();
 }
 

@@ -201,6 +201,64 @@ beam::Shape shape_of(const beam_moe_cfg& c, int64_t T) {
                      c.routed_scale};
 }
 
+// Steps after routing: align, (FP8 quantisation,) gate/up, down, combine, over the experts
+// [e_begin, e_begin + e_count) whose weights start at w_gate_up / w_down (and the FP8 scales).
+// `filter` makes the combine skip slots routed outside that range.
+beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, char* ws,
+                          const int32_t* ids, const float* tw, const void* x,
+                          const void* w_gate_up, const void* w_down,
+                          const float* w_gate_up_scale, const float* w_down_scale, void* out,
+                          int e_begin, int e_count, bool filter, hipStream_t st) {
+  beam::AlignTables at;
+  at.chunk_mask = reinterpret_cast<uint64_t*>(ws + L.chunk_mask);
+  at.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  at.expert_count = reinterpret_cast<int32_t*>(ws + L.expert_count);
+  at.expert_off = reinterpret_cast<int32_t*>(ws + L.expert_off);
+  at.n_blocks = reinterpret_cast<int32_t*>(ws + L.n_blocks);
+  at.blk_expert = reinterpret_cast<int32_t*>(ws + L.blk_expert);
+  at.blk_row0 = reinterpret_cast<int32_t*>(ws + L.blk_row0);
+  at.blk_rows = reinterpret_cast<int32_t*>(ws + L.blk_rows);
+  at.sorted_slot = reinterpret_cast<int32_t*>(ws + L.sorted);
+  float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
+  const beam::Shape s = shape_of(c, T);
+  const bool small = use_small_blocks(c, T);
+  const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
+
+  if (e_count > 0) {
+    LAUNCH(2, beam::launch_align(ids, at, s, L.bm, e_begin, e_count, st));
+    if (c.w_dtype == BEAM_F32) {
+      float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
+      LAUNCH(4, beam::launch_gate_up_f32(reinterpret_cast<const float*>(x),
+                                         reinterpret_cast<const float*>(w_gate_up), hbuf, at, s,
+                                         L.max_blocks, st));
+      LAUNCH(6, beam::launch_down_f32(hbuf, reinterpret_cast<const float*>(w_down), tw, ybuf, at,
+                                      s, L.max_blocks, st));
+    } else if (!fp8) {
+      uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
+      LAUNCH(4, beam::launch_gate_up(x, w_gate_up, hbuf, nullptr, nullptr, false, at, s,
+                                     L.max_blocks, small, st));
+      LAUNCH(6, beam::launch_down(hbuf, w_down, nullptr, nullptr, false, tw, ybuf, at, s,
+                                  L.max_blocks, small, st));
+    } else {
+      uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
+      uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+      float* xs = reinterpret_cast<float*>(ws + L.xs);
+      uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+      float* hs = reinterpret_cast<float*>(ws + L.hs);
+      LAUNCH(3, beam::launch_quant_rows_fp8(reinterpret_cast<const uint16_t*>(x), T, c.hidden, xq,
+                                            xs, st));
+      LAUNCH(4, beam::launch_gate_up(xq, w_gate_up, hbuf, xs, w_gate_up_scale, true, at, s,
+                                     L.max_blocks, small, st));
+      LAUNCH(5, beam::launch_quant_rows_fp8(hbuf, T * c.topk, c.d_ff, hq, hs, st));
+      LAUNCH(6, beam::launch_down(hq, w_down, hs, w_down_scale, true, tw, ybuf, at, s,
+                                  L.max_blocks, small, st));
+    }
+  }
+  LAUNCH(7, beam::launch_combine(ybuf, out, c.out_dtype == BEAM_BF16, s, filter ? ids : nullptr,
+                                 e_begin, e_begin + e_count, st));
+  return BEAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -312,52 +370,61 @@ beam_status_t beam_moe_forward(const void* x, const float* w_router, const float
   float2* sb = reinterpret_cast<float2*>(ws + L.sb);
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
   float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  beam::AlignTables at;
-  at.chunk_mask = reinterpret_cast<uint64_t*>(ws + L.chunk_mask);
-  at.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
-  at.expert_count = reinterpret_cast<int32_t*>(ws + L.expert_count);
-  at.expert_off = reinterpret_cast<int32_t*>(ws + L.expert_off);
-  at.n_blocks = reinterpret_cast<int32_t*>(ws + L.n_blocks);
-  at.blk_expert = reinterpret_cast<int32_t*>(ws + L.blk_expert);
-  at.blk_row0 = reinterpret_cast<int32_t*>(ws + L.blk_row0);
-  at.blk_rows = reinterpret_cast<int32_t*>(ws + L.blk_rows);
-  at.sorted_slot = reinterpret_cast<int32_t*>(ws + L.sorted);
-  float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
   const beam::Shape s = shape_of(c, T);
-  const bool small = use_small_blocks(c, T);
-
   LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
   LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
-  LAUNCH(2, beam::launch_align(ids, at, s, L.bm, st));
-  if (c.w_dtype == BEAM_F32) {
-    float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
-    LAUNCH(4, beam::launch_gate_up_f32(reinterpret_cast<const float*>(x),
-                                       reinterpret_cast<const float*>(w_gate_up), hbuf, at, s,
-                                       L.max_blocks, st));
-    LAUNCH(6, beam::launch_down_f32(hbuf, reinterpret_cast<const float*>(w_down), tw, ybuf, at, s,
-                                    L.max_blocks, st));
-  } else if (!fp8) {
-    uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
-    LAUNCH(4, beam::launch_gate_up(x, w_gate_up, hbuf, nullptr, nullptr, false, at, s,
-                                   L.max_blocks, small, st));
-    LAUNCH(6, beam::launch_down(hbuf, w_down, nullptr, nullptr, false, tw, ybuf, at, s,
-                                L.max_blocks, small, st));
-  } else {
-    uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
-    uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
-    float* xs = reinterpret_cast<float*>(ws + L.xs);
-    uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
-    float* hs = reinterpret_cast<float*>(ws + L.hs);
-    LAUNCH(3, beam::launch_quant_rows_fp8(reinterpret_cast<const uint16_t*>(x), T, c.hidden, xq, xs,
-                                          st));
-    LAUNCH(4, beam::launch_gate_up(xq, w_gate_up, hbuf, xs, w_gate_up_scale, true, at, s,
-                                   L.max_blocks, small, st));
-    LAUNCH(5, beam::launch_quant_rows_fp8(hbuf, T * c.topk, c.d_ff, hq, hs, st));
-    LAUNCH(6, beam::launch_down(hq, w_down, hs, w_down_scale, true, tw, ybuf, at, s, L.max_blocks,
-                                small, st));
+  return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
+                     out, 0, c.n_experts, false, st);
+}
+
+beam_status_t beam_moe_forward_routed(const void* x, const int32_t* topk_ids, const float* topk_w,
+                                      const void* w_gate_up, const void* w_down, void* out,
+                                      int64_t T, const beam_moe_cfg* cfg, int32_t expert_begin,
+                                      int32_t expert_end, const float* w_gate_up_scale,
+                                      const float* w_down_scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  beam_status_t rc = check_cfg(cfg, true);
+  if (rc != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  const beam_moe_cfg& c = *cfg;
+  if (expert_begin < 0 || expert_begin > expert_end || expert_end > c.n_experts)
+    return BEAM_ERR_SHAPE;
+  const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
+  if (!fp8 && (w_gate_up_scale || w_down_scale)) return BEAM_ERR_DTYPE;
+  if (T == 0) return BEAM_OK;
+  // an empty range has no local weights: those pointers may then be NULL
+  const bool local = expert_begin < expert_end;
+  if (!x || !topk_ids || !topk_w || !out || !workspace) return BEAM_ERR_NULL;
+  if (local && (!w_gate_up || !w_down)) return BEAM_ERR_NULL;
+  if (local && fp8 && (!w_gate_up_scale || !w_down_scale)) return BEAM_ERR_NULL;
+  const void* ptrs[] = {x, topk_ids, topk_w, w_gate_up, w_down, out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return BEAM_ERR_ALIGN;
+  if ((w_gate_up_scale && !aligned16(w_gate_up_scale)) ||
+      (w_down_scale && !aligned16(w_down_scale)))
+    return BEAM_ERR_ALIGN;
+  const Layout L = make_layout(c, T, true);
+  if (L.max_blocks > 65535) return BEAM_ERR_UNSUPPORTED;   // grid.y bound of the GEMM launches
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+
+  const size_t H = c.hidden, F = c.d_ff, TK = (size_t)(T * c.topk);
+  const size_t El = (size_t)(expert_end - expert_begin), wb = dtype_bytes(c.w_dtype);
+  std::vector<Range> ins = {rng(x, (size_t)T * H * dtype_bytes(c.x_dtype)),
+                            rng(topk_ids, sizeof(int32_t) * TK), rng(topk_w, sizeof(float) * TK),
+                            rng(w_gate_up, wb * El * 2 * F * H), rng(w_down, wb * El * H * F)};
+  if (fp8) {
+    ins.push_back(rng(w_gate_up_scale, sizeof(float) * El * 2 * F));
+    ins.push_back(rng(w_down_scale, sizeof(float) * El * H));
   }
-  LAUNCH(7, beam::launch_combine(ybuf, out, c.out_dtype == BEAM_BF16, s, st));
-  return BEAM_OK;
+  const std::vector<Range> outs = {rng(out, (size_t)T * H * dtype_bytes(c.out_dtype)),
+                                   rng(workspace, L.total)};
+  if (any_alias(ins, outs)) return BEAM_ERR_ALIAS;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return run_experts(c, T, L, reinterpret_cast<char*>(workspace), topk_ids, topk_w, x, w_gate_up,
+                     w_down, w_gate_up_scale, w_down_scale, out, expert_begin,
+                     expert_end - expert_begin, true, st);
 }
 
 beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols, uint8_t* codes,

@@ -4,19 +4,36 @@
 // [V] "vLLM 实现 Reflection Beam 501B MoE 模型 Day 0 支持" §MoE and residual stream (no shared
 // expert); [H] "Reflection 发布 501B 开源模型 Beam，Apache 2.0 许可" §专家混合 (outputs combined with
 // the normalised router weights times 2.5). A bf16 output is the round-to-nearest-even of the FP32 sum.
+// With given routes over a range of experts ([S] §Fusion Optimizations: expert IDs and weights in,
+// complete outputs back, every expert-parallel rank running its own experts) the sum covers the
+// slots routed to the range.
 #include "common.h"
 
 namespace beam {
 
+// FILTER: only slots whose id lies in [e_begin, e_end) contribute (a routed call over a range of
+// experts; the other slots' Y rows were never written); the sum then starts from +0.
+template <bool FILTER>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       void* __restrict__ out, int out_bf16,
-                                                      int64_t T, int H, int K) {
+                                                      int64_t T, int H, int K,
+                                                      const int32_t* __restrict__ ids, int e_begin,
+                                                      int e_end) {
   const int64_t t = blockIdx.x;
   const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= H) return;
   const float* y = Y + t * K * H + c;
-  floatx4 acc = *reinterpret_cast<const floatx4*>(y);
-  for (int k = 1; k < K; ++k) acc += *reinterpret_cast<const floatx4*>(y + (int64_t)k * H);
+  floatx4 acc;
+  if constexpr (FILTER) {
+    acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[t * K + k];
+      if (e >= e_begin && e < e_end) acc += *reinterpret_cast<const floatx4*>(y + (int64_t)k * H);
+    }
+  } else {
+    acc = *reinterpret_cast<const floatx4*>(y);
+    for (int k = 1; k < K; ++k) acc += *reinterpret_cast<const floatx4*>(y + (int64_t)k * H);
+  }
   if (out_bf16) {
     u32x2 p;
     p.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
@@ -28,11 +45,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_combine(const float* ybuf, void* out, bool out_bf16, const Shape& s,
-                          hipStream_t st) {
+                          const int32_t* ids, int e_begin, int e_end, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   dim3 grid((unsigned)s.T, (unsigned)ceil_div(s.H, 1024));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, ybuf, out, out_bf16 ? 1 : 0, s.T,
-                     s.H, s.K);
+  if (ids)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, st, ybuf, out, out_bf16 ? 1 : 0,
+                       s.T, s.H, s.K, ids, e_begin, e_end);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, st, ybuf, out, out_bf16 ? 1 : 0,
+                       s.T, s.H, s.K, ids, e_begin, e_end);
   return hipGetLastError();
 }
 

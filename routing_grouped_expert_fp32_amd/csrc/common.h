@@ -74,7 +74,7 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_route
 hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const Shape& s,
                                 hipStream_t st);
 hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
-                        hipStream_t st);
+                        int e_begin, int e_count, hipStream_t st);
 // bf16 or FP8 experts; FP8 needs the activation scales (per token for x, per sorted row for h)
 // and the per-output-channel weight scales.
 hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const float* x_scale,
@@ -94,5 +94,5 @@ hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols
 int small_block_rows();
 int tiled_block_rows();
 hipError_t launch_combine(const float* ybuf, void* out, bool out_bf16, const Shape& s,
-                          hipStream_t st);
+                          const int32_t* ids, int e_begin, int e_end, hipStream_t st);
 }  // namespace beam

@@ -21,7 +21,8 @@ def _declared():
 def test_header_declares_entry_points():
     names = _declared()
     for n in ["beam_moe_route", "beam_moe_forward", "beam_moe_workspace_bytes",
-              "beam_moe_route_workspace_bytes", "beam_status_string", "beam_moe_version"]:
+              "beam_moe_route_workspace_bytes", "beam_status_string", "beam_moe_version",
+              "beam_moe_forward_routed", "beam_moe_quant_fp8"]:
         assert n in names
 
 
@@ -141,3 +142,47 @@ def test_quant_fp8_validation():
     assert q(None, 4, 5120, A[1], A[2], None) == NULL
     assert q(A[0] + 2, 4, 5120, A[1], A[2], None) == ALIGN
     assert q(A[0], 4, 5120, A[0], A[2], None) == ALIAS          # codes on top of the source
+
+
+def _routed(cfg, T=32, x=A[0], ids=A[6], w=A[7], wgu=A[3], wd=A[4], out=A[5], begin=0, end=256,
+            gus=None, ds=None, ws=A[8], ws_bytes=1 << 38):
+    return bm.lib().beam_moe_forward_routed(x, ids, w, wgu, wd, out, T,
+                                            ctypes.byref(cfg) if cfg is not None else None,
+                                            begin, end, gus, ds, ws, ws_bytes, None)
+
+
+def test_forward_routed_validation():
+    c = _cfg()
+    assert "beam_moe_forward_routed" in _declared()
+    assert _routed(None) == NULL
+    assert _routed(c, ids=None) == NULL
+    assert _routed(c, w=None) == NULL
+    assert _routed(c, begin=-1) == SHAPE
+    assert _routed(c, begin=5, end=4) == SHAPE
+    assert _routed(c, end=257) == SHAPE
+    assert _routed(c, T=-1) == SHAPE
+    assert _routed(c, T=0, x=None, out=None, ws=None) == OK
+    assert _routed(c, gus=A[9]) == DTYPE
+    fp8 = _cfg(w_dtype=bm.BEAM_FP8_E4M3)
+    assert _routed(fp8) == NULL                              # fp8 needs both scale arrays
+    assert _routed(c, ids=A[6] + 4) == ALIGN
+    assert _routed(c, ws_bytes=bm.workspace_bytes(c, 32) - 1) == WS
+    assert _routed(c, out=A[6]) == ALIAS                     # out on top of the routes
+    assert _routed(c, out=A[8]) == ALIAS                     # out inside the workspace
+
+
+def test_forward_routed_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _routed(_cfg()) == DEVICE
+    assert _routed(_cfg(), begin=32, end=64) == DEVICE
+    assert _routed(_cfg(), begin=7, end=7) == DEVICE         # empty range: valid (zeros)
+
+
+def test_forward_routed_empty_range_needs_no_weights():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _routed(_cfg(), begin=9, end=9, wgu=None, wd=None) == DEVICE   # passes validation
+    assert _routed(_cfg(), begin=9, end=10, wgu=None) == NULL
