@@ -1,14 +1,17 @@
 """Benchmark of the Beam routed-MoE block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--also prefill,fp8_decode,fp8_prefill] [--no-cpu-baseline]
+                    [--also prefill,fp8_decode,fp8_prefill,routed_prefill] [--no-cpu-baseline]
 
 A step is one beam_moe_forward over one batch (router, selection, moe_align, [FP8 quantisers],
 gate/up GEMM, down GEMM, combine), inputs already resident in HBM. The timed region is bracketed by
 torch.cuda.synchronize() on both sides; per-stage HIP events recorded by the library on the call's
 stream during the same timed steps give each kernel's average duration. Prints ONE JSON line; the
 headline `value` is the --workload (decode, T=32, the configuration the metric is quoted on), the
-other workloads are reported under "also".
+other workloads are reported under "also". routed_prefill / routed_decode time
+beam_moe_forward_routed over one expert-parallel share (experts 32..63, one group) of that batch,
+with the router's routes computed once beforehand; their bytes and FLOPs count the local slots and
+experts only.
 
 roofline (dominant kernel = the gate/up grouped GEMM). Algorithmic bytes per launch = distinct
 experts touched (counted from the routing of the batch) x the expert's gate and up weights (bf16:
@@ -55,7 +58,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill"])
-    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill",
+    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill,routed_prefill",
                    help="comma list of extra workloads ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=32)
@@ -84,11 +87,18 @@ class Weights:
         return self.cache[w_dtype]
 
 
+# routed workloads: beam_moe_forward_routed over one expert-parallel share (one group of 32
+# experts, as eight ranks would hold them) of a workload's batch, with the router's routes
+ROUTED = {"routed_prefill": ("prefill", 32, 64), "routed_decode": ("decode", 32, 64)}
+
+
 def measure(bm, synthgen, torch, name, weights, steps, warmup):
-    wl = synthgen.WORKLOADS[name]
+    routed = ROUTED.get(name)
+    base = routed[0] if routed else name
+    wl = synthgen.WORKLOADS[base]
     W = weights.get(wl.w_dtype)
     d = synthgen.make_inputs(wl, device="cuda", with_experts=False,
-                             skew_delta=skew_delta() if name == "skew" else None)
+                             skew_delta=skew_delta() if base == "skew" else None)
     sh = wl.shape
     fp8 = wl.w_dtype == "fp8"
     cfg = bm.WorkloadCfg.of(sh, wl.x_dtype, wl.w_dtype)
@@ -103,6 +113,21 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
         bm.forward(d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg, out=out,
                    topk_ids_out=ids, workspace=ws, stream=stream, **scales)
 
+    n_slots = T * sh.topk
+    if routed:
+        b, e = routed[1], routed[2]
+        tw = torch.empty((T, sh.topk), dtype=torch.float32, device="cuda")
+        bm.forward(d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg, out=out,
+                   topk_ids_out=ids, topk_w_out=tw, workspace=ws, stream=stream, **scales)
+        local = {k: (v[b:e] if v is not None else None) for k, v in scales.items()}
+        wgu, wdn = W["w_gate_up"][b:e], W["w_down"][b:e]
+        torch.cuda.synchronize()
+        n_slots = int(((ids >= b) & (ids < e)).sum())
+
+        def step():  # noqa: F811
+            bm.forward_routed(d["x"], ids, tw, wgu, wdn, cfg, b, e, out=out, workspace=ws,
+                              stream=stream, **local)
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -115,20 +140,26 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
     elapsed = time.perf_counter() - t0
     bm.timing_enable(False)
     stages = bm.timing_collect()
-    distinct = int(torch.unique(ids).numel())
+    u = torch.unique(ids)
+    if routed:
+        u = u[(u >= routed[1]) & (u < routed[2])]
+    distinct = int(u.numel())
     F, H, K, E = sh.d_ff, sh.hidden, sh.topk, sh.n_experts
+    if routed:
+        E = routed[2] - routed[1]
     wb = 1 if fp8 else 2                                   # bytes per weight element
     gu_w = 2 * F * H * wb + (2 * F * 4 if fp8 else 0)      # gate+up bytes of one expert
     dn_w = H * F * wb + (H * 4 if fp8 else 0)
     x_bytes = T * H * (1 + 4.0 / H if fp8 else 2)
     gu_ms = stages["gate_up"][0] / max(stages["gate_up"][1], 1)
-    gu_bytes = distinct * gu_w + x_bytes + T * K * F * 2
-    gu_flops = 2.0 * T * K * 2 * F * H
-    flop_per_byte = (2.0 if fp8 else 1.0) * T * K / E
+    gu_bytes = distinct * gu_w + x_bytes + n_slots * F * 2
+    gu_flops = 2.0 * n_slots * 2 * F * H
+    flop_per_byte = (2.0 if fp8 else 1.0) * n_slots / E
     dt = "fp8" if fp8 else "bf16"
     ridge = PEAK_TFLOPS[dt] * 1e12 / (HBM_PEAK_GBS * 1e9)
-    layer_bytes = distinct * (gu_w + dn_w) + E * H * 4 + E * 4 + T * H * 2 + T * H * 4
-    layer_flops = 2.0 * T * K * 3 * F * H
+    router_bytes = 0 if routed else E * H * 4 + E * 4
+    layer_bytes = distinct * (gu_w + dn_w) + router_bytes + T * H * 2 + T * H * 4
+    layer_flops = 2.0 * n_slots * 3 * F * H
     ms = elapsed * 1e3 / steps
     res = {
         "workload": name, "T": T, "dtype": dt, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
@@ -141,8 +172,11 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
                     "GBps": gu_bytes / (gu_ms * 1e-3) / 1e9,
                     "TFLOPs": gu_flops / (gu_ms * 1e-3) / 1e12},
         "bound": "hbm" if flop_per_byte < ridge else "mfma",
-        "small_blocks": T * K <= 4 * E,
+        "small_blocks": T * K <= 4 * sh.n_experts,
     }
+    if routed:
+        res["routed"] = {"workload": base, "expert_begin": routed[1], "expert_end": routed[2],
+                         "local_slots": n_slots}
     del ws, out
     return res, d, ids
 

@@ -3,7 +3,8 @@
 // At decode each touched expert carries a handful of rows, so every weight byte is used once or
 // twice: the kernel is an HBM stream. WG = 4 waves x 16 output columns; each lane streams its
 // weight row(s) straight from HBM into MFMA operand registers (no LDS), 512 bytes of every row per
-// batch with all of a batch's loads issued before its MFMAs. Token rows past the block's rows are
+// batch with all of a batch's loads issued before its MFMAs (a row's last bytes short of a batch go
+// one MFMA step at a time). Token rows past the block's rows are
 // zero operands and their results are discarded.
 //   bf16: v_mfma_f32_16x16x32_bf16, lane = row (l % 16), 16 bytes at K slice 8*(l/16) of each
 //         32-deep step; 8 steps per batch.
@@ -80,7 +81,9 @@ __global__ __launch_bounds__(256) void grouped_small_kernel(
   }
   const int koff = g * M::kLaneBytes;
   floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = 0; k < row_bytes; k += kSmallBatchBytes) {
+  const int64_t full = row_bytes - row_bytes % kSmallBatchBytes;   // whole batches
+  int64_t k = 0;
+  for (; k < full; k += kSmallBatchBytes) {
     typename M::frag a[U], w0[U], w1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -94,6 +97,14 @@ __global__ __launch_bounds__(256) void grouped_small_kernel(
       acc0 = M::mma(a[u], w0[u], acc0);
       if constexpr (GATE_UP) acc1 = M::mma(a[u], w1[u], acc1);
     }
+  }
+  for (; k < row_bytes; k += M::kStepBytes) {   // tail steps (FP8 rows of 256 * odd bytes)
+    const typename M::frag w0 = M::load(bp0 + k + koff);
+    typename M::frag w1 = M::zero();
+    if constexpr (GATE_UP) w1 = M::load(bp1 + k + koff);
+    const typename M::frag a = ap ? M::load(ap + k + koff) : M::zero();
+    acc0 = M::mma(a, w0, acc0);
+    if constexpr (GATE_UP) acc1 = M::mma(a, w1, acc1);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -113,6 +124,117 @@ __global__ __launch_bounds__(256) void grouped_small_kernel(
     } else {
       const int slot = at.sorted_slot[row0 + row];
       float y = acc0[i];
+      if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
+      reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = topk_w[slot] * y;
+    }
+  }
+}
+
+// K-split variant: a WG covers 16 output columns and its 4 waves split K into quarters (4x the
+// workgroups of the column-tiled kernel, which matters when a handful of tokens touch few experts). Each wave
+// keeps two batches of loads in flight (the next batch is issued before the current one's MFMAs);
+// the four partial tiles are summed in LDS in wave order (deterministic) and wave 0 runs the
+// epilogue. Requires (row bytes / 4) % kKsBatchBytes == 0.
+template <bool FP8>
+struct KsBatch {
+  static constexpr int kBytes = 256;   // bf16: 4 steps of 64 B; FP8: 2 steps of 128 B
+};
+template <>
+struct KsBatch<true> {
+  static constexpr int kBytes = 128;   // one 128-deep FP8 step (the quarter of 2560 is 640 B)
+};
+
+template <bool GATE_UP, bool FP8>
+__global__ __launch_bounds__(256) void grouped_small_ks_kernel(
+    const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
+    const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
+    int topk, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
+  using M = SmallMath<FP8>;
+  constexpr int U = KsBatch<FP8>::kBytes / M::kStepBytes;   // MFMA steps per batch
+  constexpr int NACC = GATE_UP ? 2 : 1;
+  __shared__ floatx4 red[4][NACC][64];
+  const int b = blockIdx.y;
+  if (b >= at.n_blocks[0]) return;
+  const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int c0 = blockIdx.x * 16;
+  const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
+  const int64_t kq = row_bytes / 4, kbeg = wave * kq;
+
+  const unsigned char* ap = nullptr;
+  if (r < rows) {
+    if constexpr (GATE_UP)
+      ap = A + (int64_t)(at.sorted_slot[row0 + r] / topk) * row_bytes + kbeg;
+    else
+      ap = A + (int64_t)(row0 + r) * row_bytes + kbeg;
+  }
+  const unsigned char* bp0;
+  const unsigned char* bp1 = nullptr;
+  if constexpr (GATE_UP) {
+    bp0 = W + ((int64_t)e * 2 * Nout + c0 + r) * row_bytes + kbeg;
+    bp1 = W + ((int64_t)e * 2 * Nout + Nout + c0 + r) * row_bytes + kbeg;
+  } else {
+    bp0 = W + ((int64_t)e * Nout + c0 + r) * row_bytes + kbeg;
+  }
+  const int koff = g * M::kLaneBytes;
+  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  typename M::frag a[2][U], w0[2][U], w1[2][U];
+  auto load = [&](int buf, int64_t k) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      w0[buf][u] = M::load(bp0 + k + u * M::kStepBytes + koff);
+      if constexpr (GATE_UP) w1[buf][u] = M::load(bp1 + k + u * M::kStepBytes + koff);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      a[buf][u] = ap ? M::load(ap + k + u * M::kStepBytes + koff) : M::zero();
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc0 = M::mma(a[buf][u], w0[buf][u], acc0);
+      if constexpr (GATE_UP) acc1 = M::mma(a[buf][u], w1[buf][u], acc1);
+    }
+  };
+  constexpr int64_t BB = KsBatch<FP8>::kBytes;
+  const int nb = (int)(kq / BB);
+  load(0, 0);
+  int i = 0;
+  for (; i + 2 <= nb; i += 2) {   // two batches per trip so the buffers stay in registers
+    load(1, (int64_t)(i + 1) * BB);
+    mma(0);
+    if (i + 2 < nb) load(0, (int64_t)(i + 2) * BB);
+    mma(1);
+  }
+  if (i < nb) mma(0);   // odd count: batch nb-1 was loaded into buffer 0
+
+  red[wave][0][lane] = acc0;
+  if constexpr (GATE_UP) red[wave][1][lane] = acc1;
+  __syncthreads();
+  if (wave != 0) return;
+  floatx4 s0 = ((red[0][0][lane] + red[1][0][lane]) + red[2][0][lane]) + red[3][0][lane];
+  floatx4 s1 = s0;
+  if constexpr (GATE_UP)
+    s1 = ((red[0][1][lane] + red[1][1][lane]) + red[2][1][lane]) + red[3][1][lane];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 4 * g + q;
+    if (row >= rows) continue;
+    const int col = c0 + r;
+    if constexpr (GATE_UP) {
+      float gv = s0[q], uv = s1[q];
+      if constexpr (FP8) {
+        const float sx = a_scale[at.sorted_slot[row0 + row] / topk];
+        gv = gv * sx * w_scale[(int64_t)e * 2 * Nout + col];
+        uv = uv * sx * w_scale[(int64_t)e * 2 * Nout + Nout + col];
+      }
+      const float h = silu_f32(bf16_round(gv)) * bf16_round(uv);
+      reinterpret_cast<uint16_t*>(out)[(int64_t)(row0 + row) * Nout + col] =
+          (uint16_t)f32_to_bf16_bits(h);
+    } else {
+      const int slot = at.sorted_slot[row0 + row];
+      float y = s0[q];
       if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
       reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = topk_w[slot] * y;
     }

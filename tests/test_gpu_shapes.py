@@ -1,0 +1,50 @@
+"""GPU parity on non-Beam shapes that take the other kernel variants: a d_ff whose quarter rows are
+not whole K-split batches (the column-tiled small-block kernel), and the tiled kernel on a small
+model, in bf16 and FP8, every token against the CPU oracle."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+import routing_grouped_expert_fp32_amd as bm
+import synthgen
+from oracle import router
+
+pytestmark = pytest.mark.gpu
+
+# H 512, 32 experts in 8 groups (keep 2), top-4, d_ff 768: down rows are 1536 B (bf16) / 768 B
+# (FP8), whose quarters (384 B / 192 B) are not whole K-split batches
+SHAPE = synthgen.BeamShape(hidden=512, n_experts=32, n_groups=8, topk_groups=2, topk=4, d_ff=768)
+
+
+def _wl(w_dtype, T):
+    return dataclasses.replace(synthgen.WORKLOADS["tiny"], name=f"shape_{w_dtype}_{T}", T=T,
+                               shape=SHAPE, x_dtype="bf16", w_dtype=w_dtype, sigma_w=0.05)
+
+
+@pytest.mark.parametrize("w_dtype,T", [("bf16", 24), ("bf16", 200), ("fp8", 24), ("fp8", 200)])
+def test_small_model_all_tokens(w_dtype, T):
+    wl = _wl(w_dtype, T)
+    print("shape test", w_dtype, "T =", T, flush=True)
+    d = synthgen.make_inputs(wl, device="cuda")
+    cfg = bm.WorkloadCfg.of(SHAPE, "bf16", w_dtype)
+    ids = torch.empty((T, SHAPE.topk), dtype=torch.int32, device="cuda")
+    kw = {}
+    if w_dtype == "fp8":
+        kw = dict(w_gate_up_scale=d["w_gate_up_scale"], w_down_scale=d["w_down_scale"])
+    out = bm.forward(d["x"], d["w_router"], d["bias"], d["w_gate_up"], d["w_down"], cfg,
+                     topk_ids_out=ids, **kw)
+    torch.cuda.synchronize()
+    r = router.route(d["x"].cpu(), d["w_router"].cpu(), d["bias"].cpu(), SHAPE.n_groups,
+                     SHAPE.topk_groups, SHAPE.topk, SHAPE.routed_scale)
+    ids_c = ids.cpu().numpy()
+    rc = parity.check_routing(ids_c, router.weights(r.s, ids_c.astype(np.int64), 2.5), r)
+    assert not rc["failures"], rc
+    get = parity.expert_loader(d["w_gate_up"], d["w_down"], SHAPE.d_ff,
+                               d.get("w_gate_up_scale"), d.get("w_down_scale"))
+    err, rms = parity.check_outputs(out.cpu().numpy(), d["x"], ids_c, r, SHAPE.routed_scale, get,
+                                    w_dtype, np.arange(T))
+    print(w_dtype, T, "max|err|/rms", err, flush=True)
+    assert err <= parity.TOL[w_dtype]
