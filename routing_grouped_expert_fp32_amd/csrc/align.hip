@@ -177,9 +177,85 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Small batches (T <= kSmallRouteT = 64 tokens): the whole align in one workgroup of 1024 threads.
+// One 64-bit mask per expert (bit t: token t chose it), counts by popcount, exclusive scans over the
+// experts in LDS, the same block table and the same stable token order as the three-kernel path.
+static_assert(kSmallRouteT <= 64, "one mask word per expert");
+
+__device__ void align_small_body(const int32_t* sid, int64_t T, int E, int K, int e_begin, int BM,
+                                 const AlignTables& at) {
+  __shared__ unsigned long long mask[256];
+  __shared__ int rows_scan[256];
+  __shared__ int blks_scan[256];
+  const int tid = threadIdx.x;
+  if (tid < 256) mask[tid] = 0ull;
+  __syncthreads();
+  const int nslot = (int)T * K;
+  for (int i = tid; i < nslot; i += blockDim.x) {
+    const int e = sid[i] - e_begin;
+    if ((unsigned)e < (unsigned)E) atomicOr(&mask[e], 1ull << (i / K));
+  }
+  __syncthreads();
+  int count = 0, nb = 0;
+  if (tid < 256) {
+    count = tid < E ? __popcll(mask[tid]) : 0;
+    nb = (count + BM - 1) / BM;
+    rows_scan[tid] = count;
+    blks_scan[tid] = nb;
+  }
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int vr = 0, vb = 0;
+    if (tid < 256 && tid >= off) {
+      vr = rows_scan[tid - off];
+      vb = blks_scan[tid - off];
+    }
+    __syncthreads();
+    if (tid < 256 && tid >= off) {
+      rows_scan[tid] += vr;
+      blks_scan[tid] += vb;
+    }
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int row_start = rows_scan[tid] - count;
+    const int blk_start = blks_scan[tid] - nb;
+    at.expert_count[tid] = count;
+    at.expert_off[tid] = row_start;
+    if (tid == E - 1) {
+      at.expert_off[E] = rows_scan[tid];
+      at.n_blocks[0] = blks_scan[tid];
+    }
+    for (int i = 0; i < nb; ++i) {   // full blocks of BM rows, then the remainder
+      at.blk_expert[blk_start + i] = tid;
+      at.blk_row0[blk_start + i] = row_start + i * BM;
+      at.blk_rows[blk_start + i] = min(BM, count - i * BM);
+    }
+  }
+  for (int i = tid; i < nslot; i += blockDim.x) {
+    const int e = sid[i] - e_begin;
+    if ((unsigned)e >= (unsigned)E) continue;
+    const int t = i / K;
+    const int rank = __popcll(mask[e] & ((1ull << t) - 1ull));
+    at.sorted_slot[rows_scan[e] - __popcll(mask[e]) + rank] = i;
+  }
+}
+
+__global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __restrict__ ids,
+                                                           AlignTables at, int64_t T, int E, int K,
+                                                           int e_begin, int BM) {
+  align_small_body(ids, T, E, K, e_begin, BM, at);
+}
+
 hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
                         int e_begin, int e_count, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
+  if (s.T <= kSmallRouteT) {
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, st, ids, at, s.T, e_count, s.K,
+                       e_begin, BM);
+    return hipGetLastError();
+  }
   const int n_chunks = (int)ceil_div(s.T, kChunk);
   hipLaunchKernelGGL(align_count_kernel, dim3(n_chunks), dim3(256), 0, st, ids, at.chunk_mask,
                      at.chunk_base, s.T, e_count, s.K, e_begin);

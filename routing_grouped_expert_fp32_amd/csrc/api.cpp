@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <algorithm>
 #include <vector>
 
 #include "../../include/beam_moe.h"
@@ -59,7 +60,11 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full) {
     return o;
   };
   const int64_t E = c.n_experts, K = c.topk, TK = T * K;
-  L.sb = take(sizeof(float) * 2 * (size_t)(T * E));
+  // (s, b) pairs per token and expert, or for small batches the partial logits [H/256][T][E]
+  const int64_t sb_floats = T <= beam::kSmallRouteT
+                                ? std::max<int64_t>(2, c.hidden / 256) * T * E
+                                : 2 * T * E;
+  L.sb = take(sizeof(float) * (size_t)sb_floats);
   if (full) {
     const int64_t n_chunks = ceil_div(T, beam::kAlignChunk);
     L.bm = block_rows(c, T);
@@ -201,14 +206,7 @@ beam::Shape shape_of(const beam_moe_cfg& c, int64_t T) {
                      c.routed_scale};
 }
 
-// Steps after routing: align, (FP8 quantisation,) gate/up, down, combine, over the experts
-// [e_begin, e_begin + e_count) whose weights start at w_gate_up / w_down (and the FP8 scales).
-// `filter` makes the combine skip slots routed outside that range.
-beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, char* ws,
-                          const int32_t* ids, const float* tw, const void* x,
-                          const void* w_gate_up, const void* w_down,
-                          const float* w_gate_up_scale, const float* w_down_scale, void* out,
-                          int e_begin, int e_count, bool filter, hipStream_t st) {
+beam::AlignTables align_tables(const Layout& L, char* ws) {
   beam::AlignTables at;
   at.chunk_mask = reinterpret_cast<uint64_t*>(ws + L.chunk_mask);
   at.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
@@ -219,6 +217,18 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
   at.blk_row0 = reinterpret_cast<int32_t*>(ws + L.blk_row0);
   at.blk_rows = reinterpret_cast<int32_t*>(ws + L.blk_rows);
   at.sorted_slot = reinterpret_cast<int32_t*>(ws + L.sorted);
+  return at;
+}
+
+// Steps after routing: align, (FP8 quantisation,) gate/up, down, combine, over the experts
+// [e_begin, e_begin + e_count) whose weights start at w_gate_up / w_down (and the FP8 scales).
+// `filter` makes the combine skip slots routed outside that range.
+beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, char* ws,
+                          const int32_t* ids, const float* tw, const void* x,
+                          const void* w_gate_up, const void* w_down,
+                          const float* w_gate_up_scale, const float* w_down_scale, void* out,
+                          int e_begin, int e_count, bool filter, hipStream_t st) {
+  const beam::AlignTables at = align_tables(L, ws);
   float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
   const beam::Shape s = shape_of(c, T);
   const bool small = use_small_blocks(c, T);
@@ -319,6 +329,12 @@ beam_status_t beam_moe_route(const void* x, const float* w_router, const float* 
   char* ws = reinterpret_cast<char*>(workspace);
   float2* sb = reinterpret_cast<float2*>(ws + L.sb);
   const beam::Shape s = shape_of(c, T);
+  if (beam::use_small_route(s)) {
+    float* part = reinterpret_cast<float*>(ws + L.sb);
+    LAUNCH(0, beam::launch_router_partials(x, c.x_dtype == BEAM_BF16, w_router, part, s, st));
+    LAUNCH(1, beam::launch_router_select_partials(part, bias, topk_ids, topk_w, s, st));
+    return BEAM_OK;
+  }
   LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
   LAUNCH(1, beam::launch_router_select(sb, topk_ids, topk_w, s, st));
   return BEAM_OK;
@@ -371,8 +387,14 @@ beam_status_t beam_moe_forward(const void* x, const float* w_router, const float
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
   float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
   const beam::Shape s = shape_of(c, T);
-  LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
-  LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  if (beam::use_small_route(s)) {   // partial logits, selection summing them
+    float* part = reinterpret_cast<float*>(ws + L.sb);
+    LAUNCH(0, beam::launch_router_partials(x, c.x_dtype == BEAM_BF16, w_router, part, s, st));
+    LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
+  } else {
+    LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
+    LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  }
   return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
                      out, 0, c.n_experts, false, st);
 }

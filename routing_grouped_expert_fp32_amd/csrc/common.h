@@ -71,6 +71,15 @@ struct Shape {
 
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_router,
                                 const float* bias, float2* sb, const Shape& s, hipStream_t st);
+// batches of at most this many tokens take the small-batch routing path (use_small_route): partial
+// logits split over 256-wide hidden chunks, selection summing them, align in one workgroup
+constexpr int64_t kSmallRouteT = 64;
+int router_partial_chunks(const Shape& s);
+bool use_small_route(const Shape& s);
+hipError_t launch_router_partials(const void* x, bool x_bf16, const float* w_router, float* part,
+                                  const Shape& s, hipStream_t st);
+hipError_t launch_router_select_partials(const float* part, const float* bias, int32_t* ids,
+                                         float* w, const Shape& s, hipStream_t st);
 hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const Shape& s,
                                 hipStream_t st);
 hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,

@@ -11,9 +11,12 @@
 //   the 5120-long dot products are split into 8 partial chains per output (4 waves over K quarters,
 //   2 alternating accumulators per wave), summed in a fixed order, so the FP32 rounding error stays
 //   ~8x below a single serial chain. Output per (t, e): s = sigmoid(logit), b = s + bias[e].
-// router_select: one wave per token, no sort: group top-2 sums, group ranks by counting, then K
-//   rounds of a wave-wide argmax (xor butterfly) over the kept groups' members; ties -> lower index.
+// router_partial (small batches): the same products split over 256-wide hidden chunks into more
+//   workgroups (a handful of tokens would leave W_r streamed by a few CUs); partial logits are
+//   summed in chunk order by the selection.
+// router_select: one wave per token, no sort (route_select.h).
 #include "common.h"
+#include "route_select.h"
 
 namespace beam {
 
@@ -107,13 +110,59 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// Selection: one wave per token, 4 tokens per WG. Lane l owns experts l, l+64, l+128, l+192.
-__device__ __forceinline__ bool better(float v1, int e1, float v2, int e2) {
-  return v1 > v2 || (v1 == v2 && e1 < e2);
+// Logits for small batches (T <= kSmallRouteT): split over the hidden dimension so that enough
+// workgroups stream W_r. WG (token tile of 16, expert tile of 16, hidden chunk of 256); wave w takes
+// hidden [256 q + 64 w, 256 q + 64 w + 64), the four wave partials are summed in wave order and
+// written to part[q][t][e]; the selection sums the chunks q in order.
+template <bool XBF16>
+__global__ __launch_bounds__(256) void router_partial_kernel(const void* __restrict__ xv,
+                                                             const float* __restrict__ wr,
+                                                             float* __restrict__ part, int64_t T,
+                                                             int H, int E) {
+  __shared__ float red[4][16][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int e0 = blockIdx.y * 16, q = blockIdx.z;
+  const int r = lane & 15, g = lane >> 4;
+  const int kbeg = q * 256 + wave * 64;
+  const int64_t t = t0 + r;
+  const int64_t arow = (t < T ? t : T - 1) * H + kbeg + 4 * g;   // tail rows re-read a valid row
+  const float* bp = wr + (int64_t)(e0 + r) * H + kbeg + 4 * g;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 64; kk += 16) {
+    float a[4];
+    if constexpr (XBF16) {
+      const u32x2 p = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(xv) + arow +
+                                                      kk);
+      a[0] = bf16_lo(p.x); a[1] = bf16_hi(p.x);
+      a[2] = bf16_lo(p.y); a[3] = bf16_hi(p.y);
+    } else {
+      const floatx4 p = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(xv) +
+                                                         arow + kk);
+      a[0] = p.x; a[1] = p.y; a[2] = p.z; a[3] = p.w;
+    }
+    const floatx4 w4 = *reinterpret_cast<const floatx4*>(bp + kk);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], w4.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], w4.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], w4.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], w4.w, acc, 0, 0, 0);
+  }
+  // D layout: lane holds rows 4g..4g+3 (tokens), column r (expert)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
+  __syncthreads();
+  const int tl = threadIdx.x >> 4, el = threadIdx.x & 15;
+  if (t0 + tl < T) {
+    const float z = ((red[0][tl][el] + red[1][tl][el]) + red[2][tl][el]) + red[3][tl][el];
+    part[((int64_t)q * T + t0 + tl) * E + e0 + el] = z;
+  }
 }
 
-__global__ __launch_bounds__(256) void router_select_kernel(const float2* __restrict__ sb,
-                                                            int32_t* __restrict__ ids,
+// ---------------------------------------------------------------------------------------------
+// Selection: one wave per token, 4 tokens per WG (select_token in route_select.h).
+template <class Src>
+__global__ __launch_bounds__(256) void router_select_kernel(Src src, int32_t* __restrict__ ids,
                                                             float* __restrict__ wout, int64_t T,
                                                             int E, int G, int Gk, int K,
                                                             float scale) {
@@ -122,98 +171,12 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float2* __rest
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wave exits together; no block barrier below
-  const int gs = E / G;
-  float sv[4], bv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    if (e < E) {
-      float2 p = sb[t * E + e];
-      sv[j] = p.x;
-      bv[j] = p.y;
-      bl[wave][e] = p.y;
-    } else {
-      sv[j] = 0.f;
-      bv[j] = -INFINITY;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  // group score: sum of the two largest b of the group (duplicates count twice)
-  float myscore = -INFINITY;
-  if (lane < G) {
-    float v1 = -INFINITY, v2 = -INFINITY;
-    for (int m = 0; m < gs; ++m) {
-      const float v = bl[wave][lane * gs + m];
-      if (v > v1) {
-        v2 = v1;
-        v1 = v;
-      } else if (v > v2) {
-        v2 = v;
-      }
-    }
-    myscore = gs >= 2 ? v1 + v2 : v1;
-    gsc[wave][lane] = myscore;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  bool kept_me = false;
-  if (lane < G) {
-    int rank = 0;
-    for (int q = 0; q < G; ++q) {
-      const float o = gsc[wave][q];
-      rank += (o > myscore || (o == myscore && q < lane)) ? 1 : 0;
-    }
-    kept_me = rank < Gk;
-  }
-  const uint64_t kept = __ballot(kept_me);
-  float cv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    cv[j] = (e < E && ((kept >> (e / gs)) & 1ull)) ? bv[j] : -INFINITY;
-  }
-  int my_id = 0;
-  float my_s = 0.f, ssum = 0.f;
-  for (int k = 0; k < K; ++k) {
-    float v = cv[0];
-    int e = lane;
-#pragma unroll
-    for (int j = 1; j < 4; ++j)
-      if (cv[j] > v) {  // strict: on equal values the lower expert (smaller j) stays
-        v = cv[j];
-        e = lane + 64 * j;
-      }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(v, off);
-      const int oe = __shfl_xor(e, off);
-      if (better(ov, oe, v, e)) {
-        v = ov;
-        e = oe;
-      }
-    }
-    // every lane now holds the winner e; its owner retires it
-    const int owner = e & 63, slotj = e >> 6;
-    float s_win = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j == slotj) s_win = sv[j];
-    s_win = __shfl(s_win, owner);
-    if (lane == owner) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j == slotj) cv[j] = -INFINITY;
-    }
-    ssum += s_win;
-    if (lane == k) {
-      my_id = e;
-      my_s = s_win;
-    }
-  }
+  int id;
+  float w;
+  select_token(src, t, lane, bl[wave], gsc[wave], E, G, Gk, K, scale, id, w);
   if (lane < K) {
-    ids[t * K + lane] = my_id;
-    wout[t * K + lane] = scale * my_s / ssum;
+    ids[t * K + lane] = id;
+    wout[t * K + lane] = w;
   }
 }
 
@@ -244,9 +207,39 @@ hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const 
                                 hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(s.T, 4));
-  hipLaunchKernelGGL(router_select_kernel, grid, dim3(256), 0, st, sb, ids, w, s.T, s.E, s.G,
-                     s.Gk, s.K, s.scale);
+  hipLaunchKernelGGL(router_select_kernel<ScoresFromPairs>, grid, dim3(256), 0, st,
+                     ScoresFromPairs{sb, s.E}, ids, w, s.T, s.E, s.G, s.Gk, s.K, s.scale);
   return hipGetLastError();
 }
+
+int router_partial_chunks(const Shape& s) { return s.H / 256; }
+
+bool use_small_route(const Shape& s) {
+  return s.T <= kSmallRouteT && router_partial_chunks(s) <= kMaxChunks;
+}
+
+hipError_t launch_router_select_partials(const float* part, const float* bias, int32_t* ids,
+                                         float* w, const Shape& s, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(s.T, 4));
+  const ScoresFromPartials src{part, bias, router_partial_chunks(s), s.T, s.E};
+  hipLaunchKernelGGL(router_select_kernel<ScoresFromPartials>, grid, dim3(256), 0, st, src, ids, w,
+                     s.T, s.E, s.G, s.Gk, s.K, s.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_partials(const void* x, bool x_bf16, const float* w_router, float* part,
+                                  const Shape& s, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(s.T, 16), s.E / 16, router_partial_chunks(s));
+  if (x_bf16)
+    hipLaunchKernelGGL(router_partial_kernel<true>, grid, dim3(256), 0, st, x, w_router, part,
+                       s.T, s.H, s.E);
+  else
+    hipLaunchKernelGGL(router_partial_kernel<false>, grid, dim3(256), 0, st, x, w_router, part,
+                       s.T, s.H, s.E);
+  return hipGetLastError();
+}
+
 
 }  // namespace beam
