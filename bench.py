@@ -1,7 +1,8 @@
 """Benchmark of the Beam routed-MoE block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--also prefill,fp8_decode,fp8_prefill,routed_prefill] [--no-cpu-baseline]
+                    [--also prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill]
+                    [--no-cpu-baseline]
 
 A step is one beam_moe_forward over one batch (router, selection, moe_align, [FP8 quantisers],
 gate/up GEMM, down GEMM, combine), inputs already resident in HBM. The timed region is bracketed by
@@ -11,7 +12,8 @@ headline `value` is the --workload (decode, T=32, the configuration the metric i
 other workloads are reported under "also". routed_prefill / routed_decode time
 beam_moe_forward_routed over one expert-parallel share (experts 32..63, one group) of that batch,
 with the router's routes computed once beforehand; their bytes and FLOPs count the local slots and
-experts only.
+experts only. dense_prefill times beam_dense_mlp_forward on Beam's dense layer (d_ff 20480) at
+T=8192.
 
 roofline (dominant kernel = the gate/up grouped GEMM). Algorithmic bytes per launch = distinct
 experts touched (counted from the routing of the batch) x the expert's gate and up weights (bf16:
@@ -58,7 +60,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill"])
-    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill,routed_prefill",
+    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill",
                    help="comma list of extra workloads ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=32)
@@ -181,6 +183,48 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
     return res, d, ids
 
 
+def measure_dense(bm, synthgen, torch, T, steps, warmup):
+    """Beam's dense SwiGLU layer (hidden 5120, d_ff 20480, bf16) at T tokens: beam_dense_mlp_forward
+    per step. MFMA-bound at prefill sizes: FLOP = 2 * T * 3 * hidden * d_ff."""
+    d = synthgen.make_dense(T, device="cuda")
+    H, F = d["hidden"], d["d_ff"]
+    ws = torch.empty(bm.dense_workspace_bytes(H, F, bm.BEAM_BF16, T), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bm.dense_mlp(d["x"], d["w_gate_up"], d["w_down"], out=out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    bm.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    bm.timing_enable(False)
+    stages = bm.timing_collect()
+    ms = elapsed * 1e3 / steps
+    flops = 2.0 * T * 3 * H * F
+    gu_ms = stages["gate_up"][0] / max(stages["gate_up"][1], 1)
+    gu_flops = 2.0 * T * 2 * F * H
+    res = {"workload": f"dense_prefill: Beam dense SwiGLU layer, T={T}, hidden {H}, d_ff {F}, bf16",
+           "T": T, "dtype": "bf16", "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+           "layer_TFLOPs": flops / (ms * 1e-3) / 1e12,
+           "layer_frac_of_mfma_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+           "stages_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items()},
+           "roofline": {"bound": "mfma", "kernel": "gate_up: grouped_pipe_kernel<true, false>",
+                        "achieved": gu_flops / (gu_ms * 1e-3) / 1e12,
+                        "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                        "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+                        "traffic": None}}
+    del ws, out, d
+    return res
+
+
 def roofline(r, workload):
     g = r["gate_up"]
     if r["bound"] == "hbm":
@@ -190,7 +234,7 @@ def roofline(r, workload):
         pk = PEAK_TFLOPS[r["dtype"]]
         roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": pk, "unit": "TFLOP/s",
                 "frac": g["TFLOPs"] / pk}
-    kind = "small" if r["small_blocks"] else "pipe"
+    kind = "small_ks" if r["small_blocks"] else "pipe"
     roof["kernel"] = f"gate_up: grouped_{kind}_kernel<true, {str(r['dtype'] == 'fp8').lower()}>"
     roof["algorithmic_bytes_per_launch"] = g["bytes"]
     roof["traffic"] = None
@@ -254,6 +298,11 @@ def main():
           flush=True)
     extra = {}
     for name in [s for s in a.also.split(",") if s and s != a.workload]:
+        if name == "dense_prefill":
+            r = measure_dense(bm, synthgen, torch, 8192, max(5, a.steps // 5), a.warmup)
+            extra[name] = r
+            print(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+            continue
         r, _, _ = measure(bm, synthgen, torch, name, weights, max(5, a.steps // 2), a.warmup)
         r["roofline"] = roofline(r, name)
         extra[name] = r

@@ -161,6 +161,27 @@ BEAM_API beam_status_t beam_moe_forward_routed(const void* x, const int32_t* top
                                                const float* w_down_scale, void* workspace,
                                                size_t workspace_bytes, void* stream);
 
+/* A dense SwiGLU MLP layer (Beam's first three layers are dense, d_ff 20480: [V] §MoE and residual
+ * stream; [H] §专家混合), computed by the same grouped kernels as one expert that every token is
+ * routed to with weight 1, under the same numerics contract (gate/up outputs and the activation
+ * product rounded to bf16, the down projection in FP32).
+ *   x          [T][hidden] bf16
+ *   w_gate_up  [2 d_ff][hidden] w_dtype (BEAM_BF16 or BEAM_FP8_E4M3): rows [0, d_ff) gate, the rest up
+ *   w_down     [hidden][d_ff] w_dtype
+ *   out        [T][hidden] out_dtype (BEAM_F32 or BEAM_BF16): down(silu(gate x) * up x)
+ *   w_gate_up_scale [2 d_ff], w_down_scale [hidden]: FP32 per-output-channel scales for FP8 weights
+ *              (activations then quantised on the fly as in beam_moe_forward); NULL otherwise
+ *   workspace  device scratch of at least beam_dense_mlp_workspace_bytes(hidden, d_ff, w_dtype, T)
+ * Limits: hidden % 256 == 0, d_ff % 256 == 0, hidden * d_ff < 2^31. Errors as for beam_moe_forward. */
+BEAM_API beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_up,
+                                              const void* w_down, void* out, int64_t T,
+                                              int32_t hidden, int32_t d_ff, int32_t w_dtype,
+                                              int32_t out_dtype, const float* w_gate_up_scale,
+                                              const float* w_down_scale, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+BEAM_API size_t beam_dense_mlp_workspace_bytes(int32_t hidden, int32_t d_ff, int32_t w_dtype,
+                                               int64_t T);
+
 /* Dynamic FP8 E4M3 quantisation of bf16 rows, the activation step of the FP8 experts (dynamic FP8
  * checkpoints: [S] §Highlights, §BF16, NVFP4 and FP8 Model Support).
  *   src    [rows][cols] bf16 (device), cols % 8 == 0

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "BEAM_F32", "BEAM_BF16", "BEAM_FP8_E4M3", "Cfg", "make_cfg", "lib", "lib_path", "route",
     "forward", "workspace_bytes", "route_workspace_bytes", "BeamError", "timing_enable",
-    "timing_collect", "STAGES", "status_string", "quant_fp8", "forward_routed",
+    "timing_collect", "STAGES", "status_string", "quant_fp8", "forward_routed", "dense_mlp",
+    "dense_workspace_bytes",
 ]
 
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward_routed.argtypes = [vp, vp, vp, vp, vp, vp, i64, cfgp, i32, i32, vp,
                                               vp, vp, sz, vp]
         L.beam_moe_forward_routed.restype = i32
+        L.beam_dense_mlp_forward.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, vp,
+                                             sz, vp]
+        L.beam_dense_mlp_forward.restype = i32
+        L.beam_dense_mlp_workspace_bytes.argtypes = [i32, i32, i32, i64]
+        L.beam_dense_mlp_workspace_bytes.restype = sz
         L.beam_moe_quant_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
         L.beam_moe_quant_fp8.restype = i32
         _LIB = L
@@ -192,6 +198,31 @@ def forward_routed(x, topk_ids, topk_w, w_gate_up, w_down, cfg: Cfg, expert_begi
                                        _stream(stream))
     if rc != 0:
         raise BeamError(rc, "beam_moe_forward_routed")
+    return out
+
+
+def dense_workspace_bytes(hidden: int, d_ff: int, w_dtype: int, T: int) -> int:
+    return int(lib().beam_dense_mlp_workspace_bytes(hidden, d_ff, w_dtype, T))
+
+
+def dense_mlp(x, w_gate_up, w_down, out=None, out_dtype=BEAM_F32, w_gate_up_scale=None,
+              w_down_scale=None, workspace=None, stream=None):
+    """beam_dense_mlp_forward: out [T][hidden] = down(silu(gate x) * up x) for bf16 x."""
+    T, H = x.shape
+    F = w_gate_up.shape[0] // 2
+    wdt = _DT_CODE[w_gate_up.dtype]
+    if out is None:
+        odt = torch.bfloat16 if out_dtype == BEAM_BF16 else torch.float32
+        out = torch.empty((T, H), dtype=odt, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(dense_workspace_bytes(H, F, wdt, T), 16), dtype=torch.uint8,
+                                device=x.device)
+    _check_dev(x, w_gate_up, w_down, out, w_gate_up_scale, w_down_scale, workspace)
+    rc = lib().beam_dense_mlp_forward(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(out), T, H, F,
+                                      wdt, out_dtype, _ptr(w_gate_up_scale), _ptr(w_down_scale),
+                                      _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_dense_mlp_forward")
     return out
 
 

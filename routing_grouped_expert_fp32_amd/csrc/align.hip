@@ -248,6 +248,24 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
   align_small_body(ids, T, E, K, e_begin, BM, at);
 }
 
+// Routes of a dense layer run as one expert: every token's single slot goes to expert 0 with
+// weight 1 (so the down epilogue and the combine are exact copies of the MLP output).
+__global__ __launch_bounds__(256) void fill_dense_routes_kernel(int32_t* __restrict__ ids,
+                                                                float* __restrict__ w, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    ids[i] = 0;
+    w[i] = 1.0f;
+  }
+}
+
+hipError_t launch_fill_dense_routes(int32_t* ids, float* w, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_dense_routes_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
+                     ids, w, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
                         int e_begin, int e_count, hipStream_t st) {
   if (s.T == 0) return hipSuccess;

@@ -35,7 +35,7 @@ size_t dtype_bytes(int32_t dt) {
 }
 
 // Block rows of moe_align for this call: small decode-like batches stream weights through 16-row
-// blocks; larger ones use the 128-row LDS-tiled kernels. FP32 experts use 16-row blocks.
+// blocks; larger ones use the 256-row LDS-tiled kernels. FP32 experts use 16-row blocks.
 bool use_small_blocks(const beam_moe_cfg& c, int64_t T) {
   return c.w_dtype == BEAM_F32 || T * c.topk <= 4 * (int64_t)c.n_experts;
 }
@@ -447,6 +447,70 @@ beam_status_t beam_moe_forward_routed(const void* x, const int32_t* topk_ids, co
   return run_experts(c, T, L, reinterpret_cast<char*>(workspace), topk_ids, topk_w, x, w_gate_up,
                      w_down, w_gate_up_scale, w_down_scale, out, expert_begin,
                      expert_end - expert_begin, true, st);
+}
+
+// A dense SwiGLU layer as a one-expert block: E = G = Gk = K = 1, weight 1.
+beam_moe_cfg dense_cfg(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t out_dtype) {
+  return beam_moe_cfg{hidden, 1, 1, 1, 1, d_ff, 1.0f, BEAM_BF16, w_dtype, out_dtype};
+}
+
+beam_status_t check_dense(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t out_dtype,
+                          int64_t T) {
+  if (hidden <= 0 || d_ff <= 0 || T < 0) return BEAM_ERR_SHAPE;
+  if (w_dtype != BEAM_BF16 && w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
+  if (out_dtype != BEAM_F32 && out_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
+  if (hidden % 256 != 0 || d_ff % 256 != 0 || (int64_t)hidden * d_ff >= (int64_t(1) << 31) ||
+      T >= (int64_t(1) << 31))
+    return BEAM_ERR_UNSUPPORTED;
+  return BEAM_OK;
+}
+
+size_t beam_dense_mlp_workspace_bytes(int32_t hidden, int32_t d_ff, int32_t w_dtype, int64_t T) {
+  if (check_dense(hidden, d_ff, w_dtype, BEAM_F32, T) != BEAM_OK) return 0;
+  return make_layout(dense_cfg(hidden, d_ff, w_dtype, BEAM_F32), T, true).total;
+}
+
+beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_up, const void* w_down,
+                                     void* out, int64_t T, int32_t hidden, int32_t d_ff,
+                                     int32_t w_dtype, int32_t out_dtype,
+                                     const float* w_gate_up_scale, const float* w_down_scale,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  beam_status_t rc = check_dense(hidden, d_ff, w_dtype, out_dtype, T);
+  if (rc != BEAM_OK) return rc;
+  const bool fp8 = w_dtype == BEAM_FP8_E4M3;
+  if (!fp8 && (w_gate_up_scale || w_down_scale)) return BEAM_ERR_DTYPE;
+  if (T == 0) return BEAM_OK;
+  if (!x || !w_gate_up || !w_down || !out || !workspace) return BEAM_ERR_NULL;
+  if (fp8 && (!w_gate_up_scale || !w_down_scale)) return BEAM_ERR_NULL;
+  const void* ptrs[] = {x, w_gate_up, w_down, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BEAM_ERR_ALIGN;
+  if ((w_gate_up_scale && !aligned16(w_gate_up_scale)) ||
+      (w_down_scale && !aligned16(w_down_scale)))
+    return BEAM_ERR_ALIGN;
+  const beam_moe_cfg c = dense_cfg(hidden, d_ff, w_dtype, out_dtype);
+  const Layout L = make_layout(c, T, true);
+  if (L.max_blocks > 65535) return BEAM_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+  const size_t H = hidden, F = d_ff, wb = dtype_bytes(w_dtype);
+  std::vector<Range> ins = {rng(x, (size_t)T * H * 2), rng(w_gate_up, wb * 2 * F * H),
+                            rng(w_down, wb * H * F)};
+  if (fp8) {
+    ins.push_back(rng(w_gate_up_scale, sizeof(float) * 2 * F));
+    ins.push_back(rng(w_down_scale, sizeof(float) * H));
+  }
+  const std::vector<Range> outs = {rng(out, (size_t)T * H * dtype_bytes(out_dtype)),
+                                   rng(workspace, L.total)};
+  if (any_alias(ins, outs)) return BEAM_ERR_ALIAS;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* tw = reinterpret_cast<float*>(ws + L.w);
+  if (beam::launch_fill_dense_routes(ids, tw, T, st) != hipSuccess) return BEAM_ERR_LAUNCH;
+  return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
+                     out, 0, 1, false, st);
 }
 
 beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols, uint8_t* codes,

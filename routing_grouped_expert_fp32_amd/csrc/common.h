@@ -82,6 +82,7 @@ hipError_t launch_router_select_partials(const float* part, const float* bias, i
                                          float* w, const Shape& s, hipStream_t st);
 hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const Shape& s,
                                 hipStream_t st);
+hipError_t launch_fill_dense_routes(int32_t* ids, float* w, int64_t n, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
                         int e_begin, int e_count, hipStream_t st);
 // bf16 or FP8 experts; FP8 needs the activation scales (per token for x, per sorted row for h)

@@ -26,10 +26,11 @@ import torch
 
 __all__ = [
     "TENSOR_IDS", "BeamShape", "Workload", "WORKLOADS", "normal", "uniform", "fp8_rows",
-    "hot_set", "make_inputs", "normal_table",
+    "hot_set", "make_inputs", "normal_table", "make_dense", "DENSE_D_FF",
 ]
 
-TENSOR_IDS = dict(x=1, w_router=2, bias=3, w_gate_up=4, w_down=5, hot_set=6)
+TENSOR_IDS = dict(x=1, w_router=2, bias=3, w_gate_up=4, w_down=5, hot_set=6, dense_gate_up=7,
+                  dense_down=8)
 
 _M32 = 0xFFFFFFFF
 
@@ -260,3 +261,27 @@ def skew_hot_fraction_target() -> tuple:
 def nbytes_gib(t: torch.Tensor) -> float:
     return t.numel() * t.element_size() / 2 ** 30
 
+
+
+# Beam's dense MLP layers (the first three): d_ff 20480
+DENSE_D_FF = 20480
+
+
+def make_dense(T: int, hidden: int = 5120, d_ff: int = DENSE_D_FF, w_dtype: str = "bf16",
+               device="cpu", seed: int = 0, sigma_w: float = 0.02) -> dict:
+    """Inputs of one dense SwiGLU layer: x [T][hidden] bf16 N(0,1) (the same stream as the MoE
+    workloads' x), w_gate_up [2 d_ff][hidden] and w_down [hidden][d_ff] N(0, sigma_w^2) in bf16, or
+    as FP8 E4M3 codes with per-row scales (w_gate_up_scale, w_down_scale)."""
+    out = {"T": T, "hidden": hidden, "d_ff": d_ff}
+    out["x"] = normal((T, hidden), 1.0, seed, TENSOR_IDS["x"], device, torch.bfloat16)
+    if w_dtype == "fp8":
+        out["w_gate_up"], out["w_gate_up_scale"] = fp8_rows(
+            2 * d_ff, hidden, sigma_w, seed, TENSOR_IDS["dense_gate_up"], device)
+        out["w_down"], out["w_down_scale"] = fp8_rows(
+            hidden, d_ff, sigma_w, seed, TENSOR_IDS["dense_down"], device)
+    else:
+        out["w_gate_up"] = normal((2 * d_ff, hidden), sigma_w, seed, TENSOR_IDS["dense_gate_up"],
+                                  device, torch.bfloat16)
+        out["w_down"] = normal((hidden, d_ff), sigma_w, seed, TENSOR_IDS["dense_down"], device,
+                               torch.bfloat16)
+    return out

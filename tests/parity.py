@@ -19,6 +19,9 @@ from oracle import experts, router
 
 MARGIN = 1e-6
 TOL = {"bf16": 1e-2, "fp8": 5e-2, "f32": 1e-4}
+# FP8 over many outputs: 99.9th percentile of |err|/rms (the maximum there is dominated by rare
+# E4M3 boundary flips between the FP32 and FP64 paths)
+FP8_P999 = 2.5e-2
 
 
 def check_routing(ids_gpu, w_gpu, r: router.RouteResult, tokens=None, w_tol=1e-5):

@@ -186,3 +186,37 @@ def test_forward_routed_empty_range_needs_no_weights():
         pytest.skip("a GPU is present")
     assert _routed(_cfg(), begin=9, end=9, wgu=None, wd=None) == DEVICE   # passes validation
     assert _routed(_cfg(), begin=9, end=10, wgu=None) == NULL
+
+
+def _dense(T=32, x=A[0], wgu=A[3], wd=A[4], out=A[5], H=5120, F=20480, wdt=bm.BEAM_BF16,
+           odt=bm.BEAM_F32, gus=None, ds=None, ws=A[8], ws_bytes=1 << 38):
+    return bm.lib().beam_dense_mlp_forward(x, wgu, wd, out, T, H, F, wdt, odt, gus, ds, ws,
+                                           ws_bytes, None)
+
+
+def test_dense_mlp_validation():
+    names = _declared()
+    assert "beam_dense_mlp_forward" in names and "beam_dense_mlp_workspace_bytes" in names
+    assert _dense(T=-1) == SHAPE
+    assert _dense(H=0) == SHAPE
+    assert _dense(wdt=bm.BEAM_F32) == DTYPE
+    assert _dense(odt=bm.BEAM_FP8_E4M3) == DTYPE
+    assert _dense(gus=A[9]) == DTYPE                        # scales only with fp8 weights
+    assert _dense(H=5000) == UNSUP
+    assert _dense(F=20000) == UNSUP
+    assert _dense(H=65536, F=65536) == UNSUP                # hidden * d_ff >= 2^31
+    assert _dense(T=0, x=None, out=None, ws=None) == OK
+    assert _dense(x=None) == NULL
+    assert _dense(wdt=bm.BEAM_FP8_E4M3) == NULL             # fp8 needs both scale arrays
+    assert _dense(out=A[5] + 4) == ALIGN
+    need = bm.dense_workspace_bytes(5120, 20480, bm.BEAM_BF16, 32)
+    assert need > 0 and bm.dense_workspace_bytes(5000, 20480, bm.BEAM_BF16, 32) == 0
+    assert _dense(ws_bytes=need - 1) == WS
+    assert _dense(out=A[0]) == ALIAS
+
+
+def test_dense_mlp_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _dense() == DEVICE
