@@ -1,7 +1,8 @@
 """Benchmark of the Beam routed-MoE block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--also prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill]
+                    [--also prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill,
+                            boundary_prefill]
                     [--no-cpu-baseline]
 
 A step is one beam_moe_forward over one batch (router, selection, moe_align, [FP8 quantisers],
@@ -13,7 +14,8 @@ other workloads are reported under "also". routed_prefill / routed_decode time
 beam_moe_forward_routed over one expert-parallel share (experts 32..63, one group) of that batch,
 with the router's routes computed once beforehand; their bytes and FLOPs count the local slots and
 experts only. dense_prefill times beam_dense_mlp_forward on Beam's dense layer (d_ff 20480) at
-T=8192.
+T=8192. boundary_prefill times beam_moe_forward_boundary (combine fused into the post-MoE
+norm -> residual -> norm boundary) and the standalone boundary at T=8192.
 
 roofline (dominant kernel = the gate/up grouped GEMM). Algorithmic bytes per launch = distinct
 experts touched (counted from the routing of the batch) x the expert's gate and up weights (bf16:
@@ -60,7 +62,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill"])
-    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill",
+    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill,"
+                   "boundary_prefill",
                    help="comma list of extra workloads ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=32)
@@ -225,6 +228,61 @@ def measure_dense(bm, synthgen, torch, T, steps, warmup):
     return res
 
 
+def measure_boundary(bm, synthgen, torch, weights, steps, warmup):
+    """The post-MoE boundary at the prefill batch (T=8192): beam_moe_forward_boundary per step (the
+    combine fused into output norm -> depth-scaled residual -> next norm), and the standalone
+    beam_residual_boundary on an FP32 sublayer output. Both HBM-bound; algorithmic bytes per token:
+    fused stage K*H*4 (Y slots) + H*2 (h) + 2*H*2 (h', x'); standalone H*4 + H*2 + 2*H*2."""
+    wl = synthgen.WORKLOADS["prefill"]
+    W = weights.get("bf16")
+    d = synthgen.make_inputs(wl, device="cuda", with_experts=False)
+    T, H, K = wl.T, wl.shape.hidden, wl.shape.topk
+    cfg = bm.WorkloadCfg.of(wl.shape, "bf16", "bf16")
+    ws = torch.empty(bm.workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    h = synthgen.normal((T, H), 1.0, 1, 9, "cuda", torch.bfloat16)
+    gp = torch.ones(H, device="cuda")
+    gn = torch.ones(H, device="cuda")
+    h_out, x_next = torch.empty_like(h), torch.empty_like(h)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        bm.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        bm.timing_enable(False)
+        st = bm.timing_collect()
+        return el * 1e3 / n, st["combine"][0] / max(st["combine"][1], 1)
+
+    fused_ms, fused_stage = run(lambda: bm.forward_boundary(
+        d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg, h, gp, gn, 12, 1e-6,
+        h_out=h_out, x_next=x_next, workspace=ws, stream=stream), steps)
+    bm.forward(d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg, out=y,
+               workspace=ws, stream=stream)
+    _, alone = run(lambda: bm.residual_boundary(y, h, gp, gn, 12, 1e-6, h_out=h_out,
+                                                x_next=x_next, stream=stream), 4 * steps)
+    fused_bytes = T * (K * H * 4 + H * 2 + 2 * H * 2)
+    alone_bytes = T * (H * 4 + H * 2 + 2 * H * 2)
+    del ws, y
+    return {"workload": "boundary_prefill: post-MoE boundary at T=8192 (hidden 5120, top-8)",
+            "T": T, "ms_per_step": fused_ms, "tokens_per_s": T / (fused_ms * 1e-3),
+            "fused_stage_ms": fused_stage, "standalone_ms": alone,
+            "roofline": {"bound": "hbm", "kernel": "boundary_kernel<true> (combine fused)",
+                         "achieved": fused_bytes / (fused_stage * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": fused_bytes / (fused_stage * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": None},
+            "standalone_roofline": {"bound": "hbm", "kernel": "boundary_kernel<false>",
+                                    "achieved": alone_bytes / (alone * 1e-3) / 1e9,
+                                    "frac": alone_bytes / (alone * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+
 def roofline(r, workload):
     g = r["gate_up"]
     if r["bound"] == "hbm":
@@ -298,6 +356,11 @@ def main():
           flush=True)
     extra = {}
     for name in [s for s in a.also.split(",") if s and s != a.workload]:
+        if name == "boundary_prefill":
+            r = measure_boundary(bm, synthgen, torch, weights, max(5, a.steps // 5), a.warmup)
+            extra[name] = r
+            print(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+            continue
         if name == "dense_prefill":
             r = measure_dense(bm, synthgen, torch, 8192, max(5, a.steps // 5), a.warmup)
             extra[name] = r

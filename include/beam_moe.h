@@ -182,6 +182,42 @@ BEAM_API beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_
 BEAM_API size_t beam_dense_mlp_workspace_bytes(int32_t hidden, int32_t d_ff, int32_t w_dtype,
                                                int64_t T);
 
+/* Sublayer boundary: output RMSNorm of a sublayer, depth-scaled residual add, and the next sublayer's
+ * input RMSNorm, in one pass (sandwich norm and depth-scaled residuals: [V] §MoE and residual stream;
+ * the fused norm -> residual -> norm transition with FP32 math and bf16 rounding points: [V]
+ * §Agent-driven optimization item 1, [S] §Sandwich Normalization and Depth-Scaled Residuals;
+ * [H] §残差流). Per token, FP32 arithmetic, each rounding to bf16 marked bf16():
+ *   u  = bf16(y)                                      (the sublayer output in the activation dtype)
+ *   p  = bf16(u * gamma_post / sqrt(mean(u^2) + eps))
+ *   h' = bf16(bf16(sqrt((n-1)/n) * h) + bf16(p / sqrt(n)))      n = depth_n >= 1
+ *   x' = bf16(h' * gamma_next / sqrt(mean(h'^2) + eps))
+ *   y          [T][hidden] y_dtype (BEAM_F32 or BEAM_BF16): the sublayer output
+ *   h          [T][hidden] bf16: the residual stream before the add
+ *   gamma_post, gamma_next  [hidden] fp32 RMSNorm weights (output norm of this sublayer, input norm
+ *              of the next one)
+ *   h_out      [T][hidden] bf16 out: h'. May be h itself (in place); no other overlap.
+ *   x_next     [T][hidden] bf16 out: x'
+ *   depth_n    the residual add's index n (the input embedding counts as add 1)
+ *   eps        RMSNorm epsilon (>= 0; the pages do not state it)
+ * Limits: hidden % 256 == 0, hidden <= 16384. */
+BEAM_API beam_status_t beam_residual_boundary(const void* y, int32_t y_dtype, const void* h,
+                                              const float* gamma_post, const float* gamma_next,
+                                              void* h_out, void* x_next, int64_t T,
+                                              int32_t hidden, int32_t depth_n, float eps,
+                                              void* stream);
+
+/* beam_moe_forward with its combine fused into the boundary that follows the MoE sublayer (after the
+ * MoE the boundary kernel also combines the top-k expert outputs: [V] §Agent-driven optimization
+ * item 3): y is the FP32 combine of the routed experts (as `out` of beam_moe_forward), and the
+ * boundary above is applied to it. Arguments as for beam_moe_forward (x_dtype must be BEAM_BF16;
+ * out_dtype is unused) and beam_residual_boundary. */
+BEAM_API beam_status_t beam_moe_forward_boundary(
+    const void* x, const float* w_router, const float* bias, const void* w_gate_up,
+    const void* w_down, int64_t T, const beam_moe_cfg* cfg, const float* w_gate_up_scale,
+    const float* w_down_scale, const void* h, const float* gamma_post, const float* gamma_next,
+    int32_t depth_n, float eps, void* h_out, void* x_next, int32_t* topk_ids_out, float* topk_w_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Dynamic FP8 E4M3 quantisation of bf16 rows, the activation step of the FP8 experts (dynamic FP8
  * checkpoints: [S] §Highlights, §BF16, NVFP4 and FP8 Model Support).
  *   src    [rows][cols] bf16 (device), cols % 8 == 0

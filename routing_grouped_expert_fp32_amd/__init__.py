@@ -22,7 +22,7 @@ __all__ = [
     "BEAM_F32", "BEAM_BF16", "BEAM_FP8_E4M3", "Cfg", "make_cfg", "lib", "lib_path", "route",
     "forward", "workspace_bytes", "route_workspace_bytes", "BeamError", "timing_enable",
     "timing_collect", "STAGES", "status_string", "quant_fp8", "forward_routed", "dense_mlp",
-    "dense_workspace_bytes",
+    "dense_workspace_bytes", "residual_boundary", "forward_boundary",
 ]
 
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
@@ -97,6 +97,12 @@ def lib() -> ctypes.CDLL:
         L.beam_dense_mlp_forward.restype = i32
         L.beam_dense_mlp_workspace_bytes.argtypes = [i32, i32, i32, i64]
         L.beam_dense_mlp_workspace_bytes.restype = sz
+        f32 = ctypes.c_float
+        L.beam_residual_boundary.argtypes = [vp, i32, vp, vp, vp, vp, vp, i64, i32, i32, f32, vp]
+        L.beam_residual_boundary.restype = i32
+        L.beam_moe_forward_boundary.argtypes = [vp, vp, vp, vp, vp, i64, cfgp, vp, vp, vp, vp, vp,
+                                                i32, f32, vp, vp, vp, vp, vp, sz, vp]
+        L.beam_moe_forward_boundary.restype = i32
         L.beam_moe_quant_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
         L.beam_moe_quant_fp8.restype = i32
         _LIB = L
@@ -224,6 +230,49 @@ def dense_mlp(x, w_gate_up, w_down, out=None, out_dtype=BEAM_F32, w_gate_up_scal
     if rc != 0:
         raise BeamError(rc, "beam_dense_mlp_forward")
     return out
+
+
+def residual_boundary(y, h, gamma_post, gamma_next, depth_n: int, eps: float, h_out=None,
+                      x_next=None, stream=None):
+    """beam_residual_boundary: returns (h_out, x_next), both bf16 [T][hidden]."""
+    T, H = h.shape
+    if h_out is None:
+        h_out = torch.empty_like(h)
+    if x_next is None:
+        x_next = torch.empty_like(h)
+    _check_dev(y, h, gamma_post, gamma_next, h_out, x_next)
+    rc = lib().beam_residual_boundary(_ptr(y), _DT_CODE[y.dtype], _ptr(h), _ptr(gamma_post),
+                                      _ptr(gamma_next), _ptr(h_out), _ptr(x_next), T, H,
+                                      int(depth_n), float(eps), _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_residual_boundary")
+    return h_out, x_next
+
+
+def forward_boundary(x, w_router, bias, w_gate_up, w_down, cfg: Cfg, h, gamma_post, gamma_next,
+                     depth_n: int, eps: float, h_out=None, x_next=None, w_gate_up_scale=None,
+                     w_down_scale=None, topk_ids_out=None, topk_w_out=None, workspace=None,
+                     stream=None):
+    """beam_moe_forward_boundary: the MoE block with its combine fused into the following
+    norm -> residual -> norm boundary; returns (h_out, x_next)."""
+    T = x.shape[0]
+    if h_out is None:
+        h_out = torch.empty_like(h)
+    if x_next is None:
+        x_next = torch.empty_like(h)
+    nbytes = workspace_bytes(cfg, T)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check_dev(x, w_router, bias, w_gate_up, w_down, h, gamma_post, gamma_next, h_out, x_next,
+               w_gate_up_scale, w_down_scale, topk_ids_out, topk_w_out, workspace)
+    rc = lib().beam_moe_forward_boundary(
+        _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up), _ptr(w_down), T, ctypes.byref(cfg),
+        _ptr(w_gate_up_scale), _ptr(w_down_scale), _ptr(h), _ptr(gamma_post), _ptr(gamma_next),
+        int(depth_n), float(eps), _ptr(h_out), _ptr(x_next), _ptr(topk_ids_out), _ptr(topk_w_out),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_forward_boundary")
+    return h_out, x_next
 
 
 def quant_fp8(src, codes=None, scales=None, stream=None):

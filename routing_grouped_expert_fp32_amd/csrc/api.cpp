@@ -227,7 +227,8 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
                           const int32_t* ids, const float* tw, const void* x,
                           const void* w_gate_up, const void* w_down,
                           const float* w_gate_up_scale, const float* w_down_scale, void* out,
-                          int e_begin, int e_count, bool filter, hipStream_t st) {
+                          int e_begin, int e_count, bool filter, hipStream_t st,
+                          const beam::BoundaryArgs* bnd = nullptr) {
   const beam::AlignTables at = align_tables(L, ws);
   float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
   const beam::Shape s = shape_of(c, T);
@@ -264,9 +265,54 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
                                   L.max_blocks, small, st));
     }
   }
+  if (bnd) {   // combine fused into the post-MoE boundary
+    LAUNCH(7, beam::launch_boundary(*bnd, ybuf, c.topk, filter ? ids : nullptr, e_begin,
+                                    e_begin + e_count, nullptr, false, T, c.hidden, st));
+    return BEAM_OK;
+  }
   LAUNCH(7, beam::launch_combine(ybuf, out, c.out_dtype == BEAM_BF16, s, filter ? ids : nullptr,
                                  e_begin, e_begin + e_count, st));
   return BEAM_OK;
+}
+
+// Boundary arguments: validation common to both boundary entry points.
+beam_status_t make_boundary(const void* h, const float* gamma_post, const float* gamma_next,
+                            void* h_out, void* x_next, int32_t hidden, int32_t depth_n, float eps,
+                            beam::BoundaryArgs& b) {
+  if (depth_n < 1 || !(std::isfinite(eps) && eps >= 0.f)) return BEAM_ERR_SHAPE;
+  if (hidden > beam::boundary_max_hidden()) return BEAM_ERR_UNSUPPORTED;
+  if (!h || !gamma_post || !gamma_next || !h_out || !x_next) return BEAM_ERR_NULL;
+  if (!aligned16(h) || !aligned16(gamma_post) || !aligned16(gamma_next) || !aligned16(h_out) ||
+      !aligned16(x_next))
+    return BEAM_ERR_ALIGN;
+  const double n = depth_n;
+  b.h = reinterpret_cast<const uint16_t*>(h);
+  b.gamma_post = gamma_post;
+  b.gamma_next = gamma_next;
+  b.h_out = reinterpret_cast<uint16_t*>(h_out);
+  b.x_next = reinterpret_cast<uint16_t*>(x_next);
+  b.alpha = (float)std::sqrt((n - 1.0) / n);
+  b.beta = (float)(1.0 / std::sqrt(n));
+  b.eps = eps;
+  return BEAM_OK;
+}
+
+// Alias rule of the boundary outputs: h_out may be h itself (in place) but must not overlap any
+// other buffer; x_next must not overlap anything.
+bool boundary_alias(const std::vector<Range>& ins_except_h, const Range& h, const Range& h_out,
+                    const Range& x_next, const std::vector<Range>& other_outs) {
+  std::vector<Range> outs = other_outs;
+  outs.push_back(x_next);
+  if (!(h_out.lo == h.lo && h_out.hi == h.hi)) {
+    outs.push_back(h_out);
+    std::vector<Range> ins = ins_except_h;
+    ins.push_back(h);
+    return any_alias(ins, outs);
+  }
+  // in place: h (= h_out) is both; it must still be disjoint from every other buffer
+  std::vector<Range> ins = ins_except_h;
+  outs.push_back(h_out);
+  return any_alias(ins, outs);
 }
 
 }  // namespace
@@ -397,6 +443,100 @@ beam_status_t beam_moe_forward(const void* x, const float* w_router, const float
   }
   return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
                      out, 0, c.n_experts, false, st);
+}
+
+beam_status_t beam_residual_boundary(const void* y, int32_t y_dtype, const void* h,
+                                     const float* gamma_post, const float* gamma_next,
+                                     void* h_out, void* x_next, int64_t T, int32_t hidden,
+                                     int32_t depth_n, float eps, void* stream) {
+  if (T < 0 || hidden <= 0) return BEAM_ERR_SHAPE;
+  if (y_dtype != BEAM_F32 && y_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
+  if (hidden % 256 != 0 || T >= (int64_t(1) << 31)) return BEAM_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_OK;
+  beam::BoundaryArgs b;
+  beam_status_t rc = make_boundary(h, gamma_post, gamma_next, h_out, x_next, hidden, depth_n, eps,
+                                   b);
+  if (rc != BEAM_OK) return rc;
+  if (!y) return BEAM_ERR_NULL;
+  if (!aligned16(y)) return BEAM_ERR_ALIGN;
+  const size_t TH = (size_t)T * hidden;
+  const std::vector<Range> ins = {rng(y, TH * dtype_bytes(y_dtype)),
+                                  rng(gamma_post, sizeof(float) * hidden),
+                                  rng(gamma_next, sizeof(float) * hidden)};
+  if (boundary_alias(ins, rng(h, TH * 2), rng(h_out, TH * 2), rng(x_next, TH * 2), {}))
+    return BEAM_ERR_ALIAS;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  LAUNCH(7, beam::launch_boundary(b, nullptr, 0, nullptr, 0, 0, y, y_dtype == BEAM_BF16, T, hidden,
+                                  st));
+  return BEAM_OK;
+}
+
+beam_status_t beam_moe_forward_boundary(const void* x, const float* w_router, const float* bias,
+                                        const void* w_gate_up, const void* w_down, int64_t T,
+                                        const beam_moe_cfg* cfg, const float* w_gate_up_scale,
+                                        const float* w_down_scale, const void* h,
+                                        const float* gamma_post, const float* gamma_next,
+                                        int32_t depth_n, float eps, void* h_out, void* x_next,
+                                        int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  beam_status_t rc = check_cfg(cfg, true);
+  if (rc != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  const beam_moe_cfg& c = *cfg;
+  if (c.x_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;   // the residual stream is bf16
+  const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
+  if (!fp8 && (w_gate_up_scale || w_down_scale)) return BEAM_ERR_DTYPE;
+  if (T == 0) return BEAM_OK;
+  beam::BoundaryArgs bnd;
+  if ((rc = make_boundary(h, gamma_post, gamma_next, h_out, x_next, c.hidden, depth_n, eps,
+                          bnd)) != BEAM_OK)
+    return rc;
+  if (!x || !w_router || !bias || !w_gate_up || !w_down || !workspace) return BEAM_ERR_NULL;
+  if (fp8 && (!w_gate_up_scale || !w_down_scale)) return BEAM_ERR_NULL;
+  const void* ptrs[] = {x, w_router, bias, w_gate_up, w_down, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BEAM_ERR_ALIGN;
+  if ((topk_ids_out && !aligned16(topk_ids_out)) || (topk_w_out && !aligned16(topk_w_out)) ||
+      (w_gate_up_scale && !aligned16(w_gate_up_scale)) || (w_down_scale && !aligned16(w_down_scale)))
+    return BEAM_ERR_ALIGN;
+  const Layout L = make_layout(c, T, true);
+  if (L.max_blocks > 65535) return BEAM_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+  const size_t H = c.hidden, E = c.n_experts, F = c.d_ff, TK = (size_t)(T * c.topk);
+  const size_t wb = dtype_bytes(c.w_dtype);
+  std::vector<Range> ins = {rng(x, (size_t)T * H * 2), rng(w_router, sizeof(float) * E * H),
+                            rng(bias, sizeof(float) * E), rng(w_gate_up, wb * E * 2 * F * H),
+                            rng(w_down, wb * E * H * F), rng(gamma_post, sizeof(float) * H),
+                            rng(gamma_next, sizeof(float) * H)};
+  if (fp8) {
+    ins.push_back(rng(w_gate_up_scale, sizeof(float) * E * 2 * F));
+    ins.push_back(rng(w_down_scale, sizeof(float) * E * H));
+  }
+  std::vector<Range> outs = {rng(workspace, L.total)};
+  if (topk_ids_out) outs.push_back(rng(topk_ids_out, sizeof(int32_t) * TK));
+  if (topk_w_out) outs.push_back(rng(topk_w_out, sizeof(float) * TK));
+  const size_t TH2 = (size_t)T * H * 2;
+  if (boundary_alias(ins, rng(h, TH2), rng(h_out, TH2), rng(x_next, TH2), outs))
+    return BEAM_ERR_ALIAS;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  const beam::Shape s = shape_of(c, T);
+  if (beam::use_small_route(s)) {
+    float* part = reinterpret_cast<float*>(ws + L.sb);
+    LAUNCH(0, beam::launch_router_partials(x, true, w_router, part, s, st));
+    LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
+  } else {
+    LAUNCH(0, beam::launch_router_logits(x, true, w_router, bias, sb, s, st));
+    LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  }
+  return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
+                     nullptr, 0, c.n_experts, false, st, &bnd);
 }
 
 beam_status_t beam_moe_forward_routed(const void* x, const int32_t* topk_ids, const float* topk_w,

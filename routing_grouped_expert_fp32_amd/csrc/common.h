@@ -103,6 +103,21 @@ hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols
                                  float* scales, hipStream_t st);
 int small_block_rows();
 int tiled_block_rows();
+// post-norm -> depth-scaled residual -> next pre-norm (boundary.hip)
+struct BoundaryArgs {
+  const uint16_t* h;         // [T][H] bf16 residual stream in
+  const float* gamma_post;   // [H]
+  const float* gamma_next;   // [H]
+  uint16_t* h_out;           // [T][H] bf16 residual stream out (may be h)
+  uint16_t* x_next;          // [T][H] bf16 normalised input of the next sublayer
+  float alpha, beta, eps;    // sqrt((n-1)/n), 1/sqrt(n), RMSNorm epsilon
+};
+int boundary_max_hidden();
+// Y != nullptr: y = sum of the K slot rows of Y (only ids in [e_begin, e_end) when ids != nullptr);
+// otherwise y = the [T][H] fp32 or bf16 array `y`
+hipError_t launch_boundary(const BoundaryArgs& b, const float* Y, int K, const int32_t* ids,
+                           int e_begin, int e_end, const void* y, bool y_bf16, int64_t T, int H,
+                           hipStream_t st);
 hipError_t launch_combine(const float* ybuf, void* out, bool out_bf16, const Shape& s,
                           const int32_t* ids, int e_begin, int e_end, hipStream_t st);
 }  // namespace beam

@@ -220,3 +220,51 @@ def test_dense_mlp_without_gpu_reports_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _dense() == DEVICE
+
+
+def _bnd(y=A[0], ydt=bm.BEAM_F32, h=A[1], gp=A[2], gn=A[3], ho=A[4], xn=A[5], T=32, H=5120,
+         n=7, eps=1e-6):
+    return bm.lib().beam_residual_boundary(y, ydt, h, gp, gn, ho, xn, T, H, n, ctypes.c_float(eps),
+                                           None)
+
+
+def _fbnd(cfg, T=32, h=A[9], ho=A[10], xn=A[11], n=7, eps=1e-6, ws_bytes=1 << 38):
+    return bm.lib().beam_moe_forward_boundary(A[0], A[1], A[2], A[3], A[4], T,
+                                              ctypes.byref(cfg) if cfg is not None else None,
+                                              None, None, h, A[5], A[6], n, ctypes.c_float(eps),
+                                              ho, xn, None, None, A[8], ws_bytes, None)
+
+
+def test_boundary_validation():
+    names = _declared()
+    assert "beam_residual_boundary" in names and "beam_moe_forward_boundary" in names
+    assert _bnd(T=-1) == SHAPE
+    assert _bnd(n=0) == SHAPE
+    assert _bnd(eps=-1.0) == SHAPE
+    assert _bnd(eps=float("nan")) == SHAPE
+    assert _bnd(ydt=bm.BEAM_FP8_E4M3) == DTYPE
+    assert _bnd(H=5000) == UNSUP
+    assert _bnd(H=16384 + 256) == UNSUP                    # above the boundary kernel's width
+    assert _bnd(T=0, y=None, h=None, ho=None, xn=None) == OK
+    assert _bnd(y=None) == NULL
+    assert _bnd(gn=None) == NULL
+    assert _bnd(xn=A[5] + 2) == ALIGN
+    assert _bnd(xn=A[0]) == ALIAS                          # x_next on top of y
+    assert _bnd(ho=A[5]) == ALIAS                          # h_out on top of x_next
+    assert _bnd(ho=A[1] + 1024) == ALIAS                   # h_out partly over h
+    c = _cfg()
+    assert _fbnd(None) == NULL
+    assert _fbnd(_cfg(x_dtype=bm.BEAM_F32, w_dtype=bm.BEAM_F32)) == DTYPE
+    assert _fbnd(c, n=0) == SHAPE
+    assert _fbnd(c, h=None) == NULL
+    assert _fbnd(c, ws_bytes=bm.workspace_bytes(c, 32) - 1) == WS
+    assert _fbnd(c, xn=A[8]) == ALIAS                      # x_next inside the workspace
+
+
+def test_boundary_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _bnd() == DEVICE
+    assert _bnd(ho=A[1]) == DEVICE                         # in place: valid
+    assert _fbnd(_cfg()) == DEVICE
