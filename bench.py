@@ -61,7 +61,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill"])
+                   choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill",
+                            "routed_prefill", "routed_decode"])
     p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill,"
                    "boundary_prefill",
                    help="comma list of extra workloads ('' = none)")
@@ -239,7 +240,7 @@ def measure_boundary(bm, synthgen, torch, weights, steps, warmup):
     T, H, K = wl.T, wl.shape.hidden, wl.shape.topk
     cfg = bm.WorkloadCfg.of(wl.shape, "bf16", "bf16")
     ws = torch.empty(bm.workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
-    h = synthgen.normal((T, H), 1.0, 1, 9, "cuda", torch.bfloat16)
+    h = synthgen.normal((T, H), 1.0, 1, synthgen.TENSOR_IDS["residual"], "cuda", torch.bfloat16)
     gp = torch.ones(H, device="cuda")
     gn = torch.ones(H, device="cuda")
     h_out, x_next = torch.empty_like(h), torch.empty_like(h)
@@ -378,10 +379,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     cpu = None
-    wl = synthgen.WORKLOADS[a.workload]
+    wl = synthgen.WORKLOADS[ROUTED.get(a.workload, (a.workload,))[0]]
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(torch, synthgen, d, weights.get(wl.w_dtype), a.workload, a.cpu_tokens)
+        cpu = cpu_baseline(torch, synthgen, d, weights.get(wl.w_dtype),
+                           ROUTED.get(a.workload, (a.workload,))[0], a.cpu_tokens)
     sh = wl.shape
     line = {
         "metric": "MoE-layer tokens/sec (d5120, 256 exp, top-8); % of roofline",

@@ -30,7 +30,7 @@ __all__ = [
 ]
 
 TENSOR_IDS = dict(x=1, w_router=2, bias=3, w_gate_up=4, w_down=5, hot_set=6, dense_gate_up=7,
-                  dense_down=8)
+                  dense_down=8, residual=9)
 
 _M32 = 0xFFFFFFFF
 
