@@ -102,8 +102,8 @@ struct PipeMath<true> {    // FP8: one 128-deep step per stage, two 16-byte read
 // A: token rows (gate/up: x, gathered through sorted_slot; down: h in sorted-row order).
 // W: weights [E][rows][Kd]. Kd in elements. a_scale / w_scale: FP8 dequantisation scales
 // (gate/up: per token / per weight row; down: per sorted row / per weight row), unused for bf16.
-template <bool GATE_UP, bool FP8>
-__global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
+template <bool GATE_UP, bool FP8, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
     const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, int n_ctiles, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
@@ -122,6 +122,9 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
   const int b = v / n_ctiles, j = v % n_ctiles;
   const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
 
+  // waves: WAVES / 2 wave rows x 2 wave columns; wave row wm takes the 16-row sub-tiles
+  // wm, wm + WMW, ... (at most NVMAX of them), wave column wn half of the weight columns
+  constexpr int WMW = WAVES / 2, NVMAX = 16 / WMW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
   // ---- direct-load sources. Wave w issues token-row loads a = w*LA .. and weight-row loads
   // q = w*LB ..; load a covers block rows [8a, 8a+8): lane -> row 8a + lane/8, chunk slot lane%8,
   // global chunk = slot ^ row%8.
-  constexpr int LA = kPLoadsA / 4, LB = kPLoadsB / 4;
+  constexpr int LA = kPLoadsA / WAVES, LB = kPLoadsB / WAVES;
   const int lrow = lane / kPChunks;
   const int gchunk = (lane % kPChunks) ^ lrow;
   const unsigned char* asrc[LA];
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
     asrc[q] = A + arow * row_bytes + gchunk * 16;
   }
   // weight tile row br = (wave*LB + q)*8 + lrow; gate/up tiles: rows [0,128) gate, [128,256) up.
-  // A wave's LB loads cover 64 consecutive tile rows, all in one half.
+  // A wave's LB loads cover 8 LB consecutive tile rows, all in one half.
   const int br0 = wave * LB * kPRowsPerLoad + lrow;
   int64_t wrow0;
   if constexpr (GATE_UP)
@@ -170,9 +173,9 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
                                        kCachePolicyNT);
   };
 
-  floatx4 acc[8][8];
+  floatx4 acc[NVMAX][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NVMAX; ++i)
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -219,8 +222,8 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
           bw[n] = M::read(sb + grp * 16 * kPRowBytes, frag_off[s]);
         }
 #pragma unroll
-        for (int i = 0; i < NV; ++i)   // 16-row sub-tile wm + 2i of the block
-          af[i] = M::read(sa + (wm + 2 * i) * 16 * kPRowBytes, frag_off[s]);
+        for (int i = 0; i < NV; ++i)   // 16-row sub-tile wm + WMW i of the block
+          af[i] = M::read(sa + (wm + WMW * i) * 16 * kPRowBytes, frag_off[s]);
         __builtin_amdgcn_sched_barrier(0);   // all reads ahead of the MFMA chain
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -229,22 +232,33 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(
       }
     }
   };
-  // valid sub-tiles of this wave: mt = wm + 2i < ceil(rows / 16); bodies for 2, 4, 6, 8
+  // valid sub-tiles of this wave: mt = wm + WMW i < ceil(rows / 16); four loop bodies
   const int nsub = (rows + 15) >> 4;
-  const int nv = nsub > wm ? min(8, (nsub - wm + 1) >> 1) : 0;
-  if (nv > 6)
-    kloop(std::integral_constant<int, 8>{});
-  else if (nv > 4)
-    kloop(std::integral_constant<int, 6>{});
-  else if (nv > 2)
-    kloop(std::integral_constant<int, 4>{});
-  else
-    kloop(std::integral_constant<int, 2>{});
+  const int nv = nsub > wm ? min(NVMAX, (nsub - wm + WMW - 1) / WMW) : 0;
+  if constexpr (NVMAX == 8) {
+    if (nv > 6)
+      kloop(std::integral_constant<int, 8>{});
+    else if (nv > 4)
+      kloop(std::integral_constant<int, 6>{});
+    else if (nv > 2)
+      kloop(std::integral_constant<int, 4>{});
+    else
+      kloop(std::integral_constant<int, 2>{});
+  } else {
+    if (nv > 3)
+      kloop(std::integral_constant<int, 4>{});
+    else if (nv > 2)
+      kloop(std::integral_constant<int, 3>{});
+    else if (nv > 1)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 1>{});
+  }
 
   // ---- epilogue ----
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int mt = wm + 2 * i;
+  for (int i = 0; i < NVMAX; ++i) {
+    const int mt = wm + WMW * i;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = mt * 16 + 4 * g + q;
