@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kBndThreads) void boundary_kernel(
           const int e = ids[t * K + k];
           if (e < e_begin || e >= e_end) continue;
         }
-        const floatx4 yk = *reinterpret_cast<const floatx4*>(yp + (int64_t)k * H);
+        const floatx4 yk =   // read once: non-temporal
+            __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(yp + (int64_t)k * H));
         v = first ? yk : v + yk;
         first = false;
       }
