@@ -3,9 +3,11 @@
 // Used by the gate/up (fused SwiGLU epilogue) and down (weighted epilogue) steps when experts carry
 // many rows (prefill-sized batches). Design:
 //   * WG tile: up to 256 rows of one expert x 256 weight columns (gate/up: 128 gate columns and the
-//     128 matching up columns); 4 waves in a 2 x 2 grid, wave tile 128 x 128 (8 x 8 MFMA tiles of
-//     16 x 16, 256 fp32 accumulators per lane). bf16 uses v_mfma_f32_16x16x32_bf16, FP8 the
-//     16x16x128 f8f6f4 MFMA with unit block scales (operands OCP E4M3FN).
+//     128 matching up columns). WAVES = 4: a 2 x 2 wave grid, wave tile 128 x 128 (8 x 8 MFMA tiles
+//     of 16 x 16, 256 fp32 accumulators per lane, one wave per SIMD; FP8). WAVES = 8: a 4 x 2 grid,
+//     wave tile 64 x 128 (128 accumulators, two waves per SIMD, so one wave's barrier and LDS waits
+//     overlap the other's MFMAs; bf16). bf16 uses v_mfma_f32_16x16x32_bf16, FP8 the 16x16x128
+//     f8f6f4 MFMA with unit block scales (operands OCP E4M3FN).
 //   * Each stage carries 128 bytes of every row (64 bf16 or 128 FP8 values). Global -> LDS with
 //     global_load_lds_dwordx4: one wave instruction lands 1 KB = 8 rows x 128 B (whole cache
 //     lines) contiguously in LDS; each lane fetches the 16-byte chunk that belongs at its LDS slot.
@@ -15,9 +17,9 @@
 //     ahead; weights (streamed from HBM) 3 stages, issued two stages ahead, so more weight bytes
 //     are in flight (2 x 32 KB per CU); 160 KB in all. Each wave waits (s_waitcnt vmcnt) only for
 //     its own loads of the stage it reads.
-//   * Row sub-tiles are dealt to the two wave rows alternately (wave row wm takes 16-row sub-tiles
-//     wm, wm+2, ...); a wave runs one of four K-loop bodies (2, 4, 6 or 8 sub-tiles), chosen by how
-//     many of its sub-tiles hold rows, so a partly filled block costs about its rows.
+//   * Row sub-tiles are dealt to the wave rows in turn (wave row wm of WMW = WAVES/2 takes 16-row
+//     sub-tiles wm, wm+WMW, ...); a wave runs one of four K-loop bodies, chosen by how many of its
+//     sub-tiles hold rows, so a partly filled block costs about its rows.
 //   * Tile order is XCD-aware: workgroup L runs on XCD L % 8; the (block, column-tile) space is cut
 //     into 8 contiguous ranges, one per XCD, walked column-tile fastest, so the workgroups sharing
 //     a block's token rows — and the blocks of one expert sharing weight tiles — run together on
@@ -41,13 +43,12 @@ constexpr int kPChunks = kPRowBytes / 16;       // 16-byte chunks per row per st
 constexpr int kPRowsPerLoad = 64 / kPChunks;    // rows covered by one 1 KB wave load
 constexpr int kPLoadsA = kPBM / kPRowsPerLoad;  // wave loads per stage for the token rows
 constexpr int kPLoadsB = kPBN / kPRowsPerLoad;  // ... and for the weight rows
-constexpr int kPLoadsPerWave = (kPLoadsA + kPLoadsB) / 4;
 constexpr int kPAStageBytes = kPBM * kPRowBytes;
 constexpr int kPBStageBytes = kPBN * kPRowBytes;
 constexpr int kPLdsBytes = kPAStages * kPAStageBytes + kPBStages * kPBStageBytes;
 static_assert(kPChunks == 8, "swizzle below is defined for 128-byte rows");
 static_assert(kPLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kPLoadsPerWave * 3 < 64, "vmcnt range");
+static_assert((kPLoadsA + kPLoadsB) / 4 * 3 < 64, "vmcnt range (4 waves: most loads per wave)");
 
 // cache-policy operand of the direct loads: non-temporal for the weight stream (a weight tile is
 // read once per row block of its expert, so it should not push the shared token rows out of L2)
