@@ -102,7 +102,7 @@ hipError_t launch_down_f32(const float* hbuf, const float* w_dn, const float* to
 hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
                                  float* scales, hipStream_t st);
 int small_block_rows();
-int tiled_block_rows();
+int tiled_block_rows(bool fp8);   // rows per block of the tiled GEMMs
 // post-norm -> depth-scaled residual -> next pre-norm (boundary.hip)
 struct BoundaryArgs {
   const uint16_t* h;         // [T][H] bf16 residual stream in

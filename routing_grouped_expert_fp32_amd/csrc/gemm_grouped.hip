@@ -19,13 +19,8 @@
 
 namespace beam {
 
-// waves per workgroup of the tiled kernel: 8 = two waves per SIMD (128 accumulators each) for
-// bf16; FP8 keeps 4 (its 32-byte fragments would spill with two waves per SIMD)
-template <bool FP8>
-constexpr int kPipeWaves = FP8 ? 4 : 8;
-
 int small_block_rows() { return kSmallBM; }
-int tiled_block_rows() { return kPBM; }
+int tiled_block_rows(bool fp8) { return fp8 ? PipeCfg<true>::BM : PipeCfg<false>::BM; }
 
 template <bool GATE_UP, bool FP8>
 static void launch_one(const void* a, const void* w, const float* topk_w, void* out,
@@ -53,8 +48,8 @@ static void launch_one(const void* a, const void* w, const float* topk_w, void* 
   } else {
     const int n_ctiles = GATE_UP ? Nout / 128 : Nout / 256;
     const int64_t wgs = 8 * ceil_div(max_blocks * n_ctiles, 8);
-    hipLaunchKernelGGL((grouped_pipe_kernel<GATE_UP, FP8, kPipeWaves<FP8>>), dim3((unsigned)wgs),
-                       dim3(64 * kPipeWaves<FP8>), 0, st, A, W, topk_w, out, at, Kd, Nout, topk,
+    hipLaunchKernelGGL((grouped_pipe_kernel<GATE_UP, FP8>), dim3((unsigned)wgs),
+                       dim3(64 * PipeCfg<FP8>::WAVES), 0, st, A, W, topk_w, out, at, Kd, Nout, topk,
                        n_ctiles, a_scale, w_scale);
   }
 }

@@ -34,21 +34,32 @@
 
 namespace beam {
 
-constexpr int kPBM = 256;                       // max rows per block
 constexpr int kPBN = 256;                       // weight columns per WG tile
-constexpr int kPAStages = 2;                    // token-row ring depth
-constexpr int kPBStages = 3;                    // weight ring depth
 constexpr int kPRowBytes = 128;                 // bytes of one row in one stage
 constexpr int kPChunks = kPRowBytes / 16;       // 16-byte chunks per row per stage
 constexpr int kPRowsPerLoad = 64 / kPChunks;    // rows covered by one 1 KB wave load
-constexpr int kPLoadsA = kPBM / kPRowsPerLoad;  // wave loads per stage for the token rows
-constexpr int kPLoadsB = kPBN / kPRowsPerLoad;  // ... and for the weight rows
-constexpr int kPAStageBytes = kPBM * kPRowBytes;
-constexpr int kPBStageBytes = kPBN * kPRowBytes;
-constexpr int kPLdsBytes = kPAStages * kPAStageBytes + kPBStages * kPBStageBytes;
 static_assert(kPChunks == 8, "swizzle below is defined for 128-byte rows");
-static_assert(kPLdsBytes <= 160 * 1024, "LDS budget");
-static_assert((kPLoadsA + kPLoadsB) / 4 * 3 < 64, "vmcnt range (4 waves: most loads per wave)");
+
+// Per element type: block rows (BM), waves per workgroup, LDS ring depths.
+//   bf16: 320 rows (every expert of a 256-rows-per-expert batch fits one block, so its weights
+//         stream once), 8 waves (4 x 2, wave tile 80 x 128, 160 accumulators, two waves per SIMD),
+//         token rows 2 x 40 KB + weights 2 x 32 KB: both issued one stage ahead.
+//   FP8:  256 rows, 4 waves (2 x 2, wave tile 128 x 128, 256 accumulators), token rows 2 x 32 KB
+//         issued one stage ahead + weights 3 x 32 KB issued two stages ahead.
+template <bool FP8>
+struct PipeCfg {
+  static constexpr int BM = FP8 ? 256 : 320;
+  static constexpr int WAVES = FP8 ? 4 : 8;
+  static constexpr int AST = 2, BST = FP8 ? 3 : 2;
+  static constexpr int kLoadsA = BM / kPRowsPerLoad;    // wave loads per stage, token rows
+  static constexpr int kLoadsB = kPBN / kPRowsPerLoad;  // ... and weight rows
+  static constexpr int kAStageBytes = BM * kPRowBytes;
+  static constexpr int kBStageBytes = kPBN * kPRowBytes;
+  static constexpr int kLdsBytes = AST * kAStageBytes + BST * kBStageBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kLoadsA % WAVES == 0 && kLoadsB % WAVES == 0, "loads split evenly over waves");
+  static_assert((kLoadsA + kLoadsB) / WAVES * BST < 64, "vmcnt range");
+};
 
 // cache-policy operand of the direct loads: non-temporal for the weight stream (a weight tile is
 // read once per row block of its expert, so it should not push the shared token rows out of L2)
@@ -103,15 +114,17 @@ struct PipeMath<true> {    // FP8: one 128-deep step per stage, two 16-byte read
 // A: token rows (gate/up: x, gathered through sorted_slot; down: h in sorted-row order).
 // W: weights [E][rows][Kd]. Kd in elements. a_scale / w_scale: FP8 dequantisation scales
 // (gate/up: per token / per weight row; down: per sorted row / per weight row), unused for bf16.
-template <bool GATE_UP, bool FP8, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
+template <bool GATE_UP, bool FP8>
+__global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
     const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, int n_ctiles, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
   using M = PipeMath<FP8>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kPLdsBytes];
+  using C = PipeCfg<FP8>;
+  constexpr int WAVES = C::WAVES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLdsBytes];
   unsigned char* const aring = smem;
-  unsigned char* const bring = smem + kPAStages * kPAStageBytes;
+  unsigned char* const bring = smem + C::AST * C::kAStageBytes;
   // ---- tile assignment (XCD-aware) ----
   const int L = blockIdx.x;
   const int xcd = L & 7, local = L >> 3;
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
 
   // waves: WAVES / 2 wave rows x 2 wave columns; wave row wm takes the 16-row sub-tiles
   // wm, wm + WMW, ... (at most NVMAX of them), wave column wn half of the weight columns
-  constexpr int WMW = WAVES / 2, NVMAX = 16 / WMW;
+  constexpr int WMW = WAVES / 2, NVMAX = (C::BM / 16) / WMW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
@@ -133,13 +146,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
   // ---- direct-load sources. Wave w issues token-row loads a = w*LA .. and weight-row loads
   // q = w*LB ..; load a covers block rows [8a, 8a+8): lane -> row 8a + lane/8, chunk slot lane%8,
   // global chunk = slot ^ row%8.
-  constexpr int LA = kPLoadsA / WAVES, LB = kPLoadsB / WAVES;
+  constexpr int LA = C::kLoadsA / WAVES, LB = C::kLoadsB / WAVES;
   const int lrow = lane / kPChunks;
   const int gchunk = (lane % kPChunks) ^ lrow;
   const unsigned char* asrc[LA];
 #pragma unroll
   for (int q = 0; q < LA; ++q) {
-    int rr = (wave * LA + q) * kPRowsPerLoad + lrow;   // block row 0..255
+    int rr = (wave * LA + q) * kPRowsPerLoad + lrow;   // block row 0..BM-1
     if (rr >= rows) rr = rows - 1;                      // padding rows re-read a valid row
     const int64_t arow =
         GATE_UP ? (int64_t)(at.sorted_slot[row0 + rr] / topk) : (int64_t)(row0 + rr);
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
   const int64_t bstep = (int64_t)kPRowsPerLoad * row_bytes;   // bytes between consecutive loads
 
   auto issue_a = [&](int stage) {
-    unsigned char* base = aring + (stage % kPAStages) * kPAStageBytes;
+    unsigned char* base = aring + (stage % C::AST) * C::kAStageBytes;
     const int kb = stage * kPRowBytes;
 #pragma unroll
     for (int q = 0; q < LA; ++q)
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
                                        (lds_void_t*)(base + (wave * LA + q) * 1024), 16, 0, 0);
   };
   auto issue_b = [&](int stage) {
-    unsigned char* base = bring + (stage % kPBStages) * kPBStageBytes;
+    unsigned char* base = bring + (stage % C::BST) * C::kBStageBytes;
     const int kb = stage * kPRowBytes;
 #pragma unroll
     for (int q = 0; q < LB; ++q)
@@ -183,10 +196,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
   // Issue order: prologue A(0), B(0), B(1); iteration kt issues A(kt+1), B(kt+2). Entering
   // iteration kt the wave's queue ends with B(kt), A(kt), B(kt+1): all but the youngest LB loads
   // must have completed.
+  // Issue order. BST == 3: prologue A(0), B(0), B(1); iteration kt issues A(kt+1), B(kt+2);
+  // entering iteration kt the wave's queue ends with B(kt), A(kt), B(kt+1): all but the youngest
+  // LB loads must have completed. BST == 2: prologue A(0), B(0); iteration kt issues A(kt+1),
+  // B(kt+1) after its barrier, so entering it everything issued must have completed.
   const int nk = (int)(row_bytes / kPRowBytes);
   issue_a(0);
   issue_b(0);
-  if (1 < nk) issue_b(1);
+  if constexpr (C::BST == 3)
+    if (1 < nk) issue_b(1);
 
   // fragment byte offsets of this lane inside a 16-row group, per MFMA step of a stage:
   // row r = lane % 16, chunk M::chunk(step, lane / 16, half) (swizzled)
@@ -201,15 +219,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
   auto kloop = [&](auto nv_tag) {
     constexpr int NV = decltype(nv_tag)::value;
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk)
+      if (C::BST == 3 && kt + 1 < nk)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(LB));   // B(kt+1) may stay in flight
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_ring_barrier();
       if (kt + 1 < nk) issue_a(kt + 1);
-      if (kt + 2 < nk) issue_b(kt + 2);
-      const unsigned char* sa = aring + (kt % kPAStages) * kPAStageBytes;
-      const unsigned char* sb = bring + (kt % kPBStages) * kPBStageBytes;
+      if constexpr (C::BST == 3) {
+        if (kt + 2 < nk) issue_b(kt + 2);
+      } else {
+        if (kt + 1 < nk) issue_b(kt + 1);
+      }
+      const unsigned char* sa = aring + (kt % C::AST) * C::kAStageBytes;
+      const unsigned char* sb = bring + (kt % C::BST) * C::kBStageBytes;
 #pragma unroll
       for (int s = 0; s < M::kSteps; ++s) {
         typename M::frag bw[8], af[NV];
@@ -246,14 +268,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void grouped_pipe_kernel(
     else
       kloop(std::integral_constant<int, 2>{});
   } else {
-    if (nv > 3)
+    static_assert(NVMAX == 5, "loop bodies for 5 sub-tiles per wave");
+    if (nv > 4)
+      kloop(std::integral_constant<int, 5>{});
+    else if (nv > 3)
       kloop(std::integral_constant<int, 4>{});
     else if (nv > 2)
       kloop(std::integral_constant<int, 3>{});
-    else if (nv > 1)
-      kloop(std::integral_constant<int, 2>{});
     else
-      kloop(std::integral_constant<int, 1>{});
+      kloop(std::integral_constant<int, 2>{});
   }
 
   // ---- epilogue ----
