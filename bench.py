@@ -1,8 +1,8 @@
 """Benchmark of the Beam routed-MoE block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--also prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill,
-                            boundary_prefill]
+                    [--also prefill,skew,fp8_decode,fp8_prefill,routed_prefill,
+                            dense_prefill,boundary_prefill]
                     [--no-cpu-baseline]
 
 A step is one beam_moe_forward over one batch (router, selection, moe_align, [FP8 quantisers],
@@ -10,7 +10,8 @@ gate/up GEMM, down GEMM, combine), inputs already resident in HBM. The timed reg
 torch.cuda.synchronize() on both sides; per-stage HIP events recorded by the library on the call's
 stream during the same timed steps give each kernel's average duration. Prints ONE JSON line; the
 headline `value` is the --workload (decode, T=32, the configuration the metric is quoted on), the
-other workloads are reported under "also". routed_prefill / routed_decode time
+other workloads are reported under "also". skew is the T=32768 batch whose correction bias puts
+40% of the slots on 16 hot experts (about 6.5K rows each, MFMA-bound). routed_prefill / routed_decode time
 beam_moe_forward_routed over one expert-parallel share (experts 32..63, one group) of that batch,
 with the router's routes computed once beforehand; their bytes and FLOPs count the local slots and
 experts only. dense_prefill times beam_dense_mlp_forward on Beam's dense layer (d_ff 20480) at
@@ -63,8 +64,8 @@ def parse():
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill",
                             "routed_prefill", "routed_decode"])
-    p.add_argument("--also", default="prefill,fp8_decode,fp8_prefill,routed_prefill,dense_prefill,"
-                   "boundary_prefill",
+    p.add_argument("--also", default="prefill,skew,fp8_decode,fp8_prefill,routed_prefill,"
+                   "dense_prefill,boundary_prefill",
                    help="comma list of extra workloads ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=32)
