@@ -7,8 +7,10 @@
 
 A step is one beam_moe_forward over one batch (router, selection, moe_align, [FP8 quantisers],
 gate/up GEMM, down GEMM, combine), inputs already resident in HBM. The timed region is bracketed by
-torch.cuda.synchronize() on both sides; per-stage HIP events recorded by the library on the call's
-stream during the same timed steps give each kernel's average duration. Prints ONE JSON line; the
+torch.cuda.synchronize() on both sides; inside it the library records HIP events on the call's
+stream around the gate/up GEMM only (the roofline kernel), which gives that kernel's average
+duration without event records between the other kernels; stages_ms comes from a second,
+instrumented pass of the same steps with every stage recorded. Prints ONE JSON line; the
 headline `value` is the --workload (decode, T=32, the configuration the metric is quoted on), the
 other workloads are reported under "also". skew is the T=32768 batch whose correction bias puts
 40% of the slots on 16 hot experts (about 6.5K rows each, MFMA-bound). routed_prefill / routed_decode time
@@ -94,6 +96,33 @@ class Weights:
         return self.cache[w_dtype]
 
 
+def timed_steps(bm, torch, step, steps, warmup, stage):
+    """Warm up, then time `steps` calls with the wall clock while the library records HIP events
+    around `stage` only (one event pair per call on the call's stream, so no event records sit
+    between the other kernels); then a second, instrumented pass of the same calls records every
+    stage for the breakdown. Returns (ms per step, average ms of `stage` in the timed steps,
+    {stage: average ms} of the instrumented pass)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    bm.timing_enable(True, stages=[stage])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    bm.timing_enable(False)
+    tot, cnt = bm.timing_collect()[stage]
+    bm.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    bm.timing_enable(False)
+    stages = {k: (v[0] / v[1] if v[1] else None) for k, v in bm.timing_collect().items()}
+    return elapsed * 1e3 / steps, tot / max(cnt, 1), stages
+
+
 # routed workloads: beam_moe_forward_routed over one expert-parallel share (one group of 32
 # experts, as eight ranks would hold them) of a workload's batch, with the router's routes
 ROUTED = {"routed_prefill": ("prefill", 32, 64), "routed_decode": ("decode", 32, 64)}
@@ -135,18 +164,7 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
             bm.forward_routed(d["x"], ids, tw, wgu, wdn, cfg, b, e, out=out, workspace=ws,
                               stream=stream, **local)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    bm.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    bm.timing_enable(False)
-    stages = bm.timing_collect()
+    ms, gu_ms, stages_ms = timed_steps(bm, torch, step, steps, warmup, "gate_up")
     u = torch.unique(ids)
     if routed:
         u = u[(u >= routed[1]) & (u < routed[2])]
@@ -158,7 +176,6 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
     gu_w = 2 * F * H * wb + (2 * F * 4 if fp8 else 0)      # gate+up bytes of one expert
     dn_w = H * F * wb + (H * 4 if fp8 else 0)
     x_bytes = T * H * (1 + 4.0 / H if fp8 else 2)
-    gu_ms = stages["gate_up"][0] / max(stages["gate_up"][1], 1)
     gu_bytes = distinct * gu_w + x_bytes + n_slots * F * 2
     gu_flops = 2.0 * n_slots * 2 * F * H
     flop_per_byte = (2.0 if fp8 else 1.0) * n_slots / E
@@ -167,14 +184,13 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
     router_bytes = 0 if routed else E * H * 4 + E * 4
     layer_bytes = distinct * (gu_w + dn_w) + router_bytes + T * H * 2 + T * H * 4
     layer_flops = 2.0 * n_slots * 3 * F * H
-    ms = elapsed * 1e3 / steps
     res = {
         "workload": name, "T": T, "dtype": dt, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
         "layer_TBps": layer_bytes / (ms * 1e-3) / 1e12,
         "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
         "layer_frac_of_mfma_peak": layer_flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[dt],
         "distinct_experts": distinct,
-        "stages_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items()},
+        "stages_ms": stages_ms,
         "gate_up": {"ms": gu_ms, "bytes": gu_bytes, "flops": gu_flops,
                     "GBps": gu_bytes / (gu_ms * 1e-3) / 1e9,
                     "TFLOPs": gu_flops / (gu_ms * 1e-3) / 1e12},
@@ -201,26 +217,14 @@ def measure_dense(bm, synthgen, torch, T, steps, warmup):
     def step():
         bm.dense_mlp(d["x"], d["w_gate_up"], d["w_down"], out=out, workspace=ws, stream=stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    bm.timing_enable(True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    bm.timing_enable(False)
-    stages = bm.timing_collect()
-    ms = elapsed * 1e3 / steps
+    ms, gu_ms, stages_ms = timed_steps(bm, torch, step, steps, warmup, "gate_up")
     flops = 2.0 * T * 3 * H * F
-    gu_ms = stages["gate_up"][0] / max(stages["gate_up"][1], 1)
     gu_flops = 2.0 * T * 2 * F * H
     res = {"workload": f"dense_prefill: Beam dense SwiGLU layer, T={T}, hidden {H}, d_ff {F}, bf16",
            "T": T, "dtype": "bf16", "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
            "layer_TFLOPs": flops / (ms * 1e-3) / 1e12,
            "layer_frac_of_mfma_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
-           "stages_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in stages.items()},
+           "stages_ms": stages_ms,
            "roofline": {"bound": "mfma", "kernel": "gate_up: grouped_pipe_kernel<true, false>",
                         "achieved": gu_flops / (gu_ms * 1e-3) / 1e12,
                         "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
@@ -248,19 +252,9 @@ def measure_boundary(bm, synthgen, torch, weights, steps, warmup):
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def run(fn, n):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        bm.timing_enable(True)
-        t0 = time.perf_counter()
-        for _ in range(n):
-            fn()
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        bm.timing_enable(False)
-        st = bm.timing_collect()
-        return el * 1e3 / n, st["combine"][0] / max(st["combine"][1], 1)
+    def run(fn, n):   # the boundary kernel is the library's combine stage
+        ms, stage_ms, _ = timed_steps(bm, torch, fn, n, warmup, "combine")
+        return ms, stage_ms
 
     fused_ms, fused_stage = run(lambda: bm.forward_boundary(
         d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg, h, gp, gn, 12, 1e-6,

@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_version.restype = i32
         L.beam_moe_timing_enable.argtypes = [i32]
         L.beam_moe_timing_enable.restype = None
+        L.beam_moe_timing_stages.argtypes = [ctypes.c_uint32]
+        L.beam_moe_timing_stages.restype = None
         L.beam_moe_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(i32), i32]
         L.beam_moe_timing_collect.restype = i32
@@ -290,7 +292,11 @@ def quant_fp8(src, codes=None, scales=None, stream=None):
     return codes, scales
 
 
-def timing_enable(on: bool = True) -> None:
+def timing_enable(on: bool = True, stages=None) -> None:
+    """Turn stage timing on or off; `stages` (names from STAGES) limits which stages record events
+    (None: all)."""
+    mask = 0xFFFFFFFF if stages is None else sum(1 << STAGES.index(n) for n in stages)
+    lib().beam_moe_timing_stages(mask)
     lib().beam_moe_timing_enable(1 if on else 0)
 
 

@@ -169,13 +169,14 @@ struct TimingRec {
 };
 std::vector<TimingRec> g_recs;
 bool g_timing = false;
+uint32_t g_timing_mask = ~0u;
 
 struct StageTimer {
   int stage;
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
   StageTimer(int s, hipStream_t stream) : stage(s), st(stream) {
-    if (!g_timing) return;
+    if (!g_timing || !((g_timing_mask >> stage) & 1u)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
       a = b = nullptr;
       return;
@@ -675,6 +676,8 @@ beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols, ui
 }
 
 void beam_moe_timing_enable(int32_t enable) { g_timing = enable != 0; }
+
+void beam_moe_timing_stages(uint32_t stage_mask) { g_timing_mask = stage_mask; }
 
 int32_t beam_moe_timing_collect(double* total_ms, int32_t* launches, int32_t n_stages) {
   for (int i = 0; i < n_stages && i < kNumStages; ++i) {

@@ -1,0 +1,78 @@
+"""Runtime behaviour of the library through the C ABI: a forward step captured in a HIP graph replays
+to the eager result (a call launches kernels on the caller's stream and nothing else: no allocation,
+memset or synchronisation), and the stage-timing mask records only the selected stages."""
+import dataclasses
+
+import pytest
+import torch
+
+import routing_grouped_expert_fp32_amd as bm
+import synthgen
+
+pytestmark = pytest.mark.gpu
+
+# H 512, 32 experts in 8 groups (keep 2), top-4, d_ff 768: T=8 takes the small-block kernels,
+# T=700 (~87 rows per expert) the tiled ones
+SHAPE = synthgen.BeamShape(hidden=512, n_experts=32, n_groups=8, topk_groups=2, topk=4, d_ff=768)
+
+
+def _case(w_dtype, T):
+    wl = dataclasses.replace(synthgen.WORKLOADS["tiny"], name=f"runtime_{w_dtype}_{T}", T=T,
+                             shape=SHAPE, x_dtype="bf16", w_dtype=w_dtype, sigma_w=0.05)
+    d = synthgen.make_inputs(wl, device="cuda")
+    cfg = bm.WorkloadCfg.of(SHAPE, "bf16", w_dtype)
+    kw = {}
+    if w_dtype == "fp8":
+        kw = dict(w_gate_up_scale=d["w_gate_up_scale"], w_down_scale=d["w_down_scale"])
+    ws = torch.empty(bm.workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, SHAPE.hidden), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, SHAPE.topk), dtype=torch.int32, device="cuda")
+
+    def run(stream=None):
+        bm.forward(d["x"], d["w_router"], d["bias"], d["w_gate_up"], d["w_down"], cfg, out=out,
+                   topk_ids_out=ids, workspace=ws, stream=stream, **kw)
+
+    return run, out, ids
+
+
+@pytest.mark.parametrize("w_dtype,T", [("bf16", 8), ("bf16", 700), ("fp8", 700)])
+def test_graph_replay_equals_eager(w_dtype, T):
+    print("graph capture", w_dtype, "T =", T, flush=True)
+    run, out, ids = _case(w_dtype, T)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run(s)
+    torch.cuda.synchronize()
+    ref, ref_ids = out.clone(), ids.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(s)
+    torch.cuda.synchronize()
+    for i in range(3):   # eager work and a synchronisation between the replays
+        out.fill_(float("nan"))
+        ids.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(ids, ref_ids), f"replay {i}"
+
+
+def test_timing_stage_mask():
+    run, _, _ = _case("bf16", 64)
+    run()
+    torch.cuda.synchronize()
+    bm.timing_enable(True, stages=["gate_up"])
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    bm.timing_enable(False)
+    st = bm.timing_collect()
+    assert st["gate_up"][1] == 3 and st["gate_up"][0] > 0
+    assert all(n == 0 for k, (_, n) in st.items() if k != "gate_up"), st
+    bm.timing_enable(True)
+    run()
+    torch.cuda.synchronize()
+    bm.timing_enable(False)
+    st = bm.timing_collect()
+    for k in ("router_logits", "router_select", "moe_align", "gate_up", "down", "combine"):
+        assert st[k][1] == 1, (k, st)
