@@ -2,24 +2,24 @@
 //
 // Used by the gate/up (fused SwiGLU epilogue) and down (weighted epilogue) steps when experts carry
 // many rows (prefill-sized batches). Design:
-//   * WG tile: up to 256 rows of one expert x 256 weight columns (gate/up: 128 gate columns and the
-//     128 matching up columns). WAVES = 4: a 2 x 2 wave grid, wave tile 128 x 128 (8 x 8 MFMA tiles
-//     of 16 x 16, 256 fp32 accumulators per lane, one wave per SIMD; FP8). WAVES = 8: a 4 x 2 grid,
-//     wave tile 64 x 128 (128 accumulators, two waves per SIMD, so one wave's barrier and LDS waits
-//     overlap the other's MFMAs; bf16). bf16 uses v_mfma_f32_16x16x32_bf16, FP8 the 16x16x128
-//     f8f6f4 MFMA with unit block scales (operands OCP E4M3FN).
+//   * WG tile: BM rows of one expert (bf16 320, FP8 256) x 256 weight columns (gate/up: 128 gate
+//     columns and the 128 matching up columns), 8 waves in a 4 x 2 grid, two per SIMD, so one
+//     wave's barrier and LDS waits overlap the other's MFMAs. Wave tile 80 x 128 (bf16, 160 fp32
+//     accumulators per lane) or 64 x 128 (FP8, 128 accumulators; its 8-register weight fragments
+//     are read in two halves). bf16 uses v_mfma_f32_16x16x32_bf16, FP8 the 16x16x128 f8f6f4 MFMA
+//     with unit block scales (operands OCP E4M3FN).
 //   * Each stage carries 128 bytes of every row (64 bf16 or 128 FP8 values). Global -> LDS with
 //     global_load_lds_dwordx4: one wave instruction lands 1 KB = 8 rows x 128 B (whole cache
 //     lines) contiguously in LDS; each lane fetches the 16-byte chunk that belongs at its LDS slot.
 //     Chunk c of row r is stored at chunk position c ^ (r & 7), so the 16 rows a fragment read
 //     touches fall on distinct banks.
 //   * Separate LDS rings: token rows (L2-resident, short latency) 2 stages, issued one stage
-//     ahead; weights (streamed from HBM) 3 stages, issued two stages ahead, so more weight bytes
-//     are in flight (2 x 32 KB per CU); 160 KB in all. Each wave waits (s_waitcnt vmcnt) only for
-//     its own loads of the stage it reads.
-//   * Row sub-tiles are dealt to the wave rows in turn (wave row wm of WMW = WAVES/2 takes 16-row
-//     sub-tiles wm, wm+WMW, ...); a wave runs one of four K-loop bodies, chosen by how many of its
-//     sub-tiles hold rows, so a partly filled block costs about its rows.
+//     ahead; weights (streamed from HBM) 2 stages issued one stage ahead (bf16: 2 x 40 KB + 2 x
+//     32 KB) or 3 stages issued two stages ahead (FP8: 2 x 32 KB + 3 x 32 KB = 160 KB). Each wave
+//     waits (s_waitcnt vmcnt) only for its own loads of the stage it reads.
+//   * Row sub-tiles are dealt to the wave rows in turn (wave row wm of 4 takes 16-row sub-tiles
+//     wm, wm+4, ...); a wave runs one of four K-loop bodies, chosen by how many of its sub-tiles
+//     hold rows, so a partly filled block costs about its rows.
 //   * Tile order is XCD-aware: workgroup L runs on XCD L % 8; the (block, column-tile) space is cut
 //     into 8 contiguous ranges, one per XCD, walked column-tile fastest, so the workgroups sharing
 //     a block's token rows — and the blocks of one expert sharing weight tiles — run together on
@@ -44,12 +44,13 @@ static_assert(kPChunks == 8, "swizzle below is defined for 128-byte rows");
 //   bf16: 320 rows (every expert of a 256-rows-per-expert batch fits one block, so its weights
 //         stream once), 8 waves (4 x 2, wave tile 80 x 128, 160 accumulators, two waves per SIMD),
 //         token rows 2 x 40 KB + weights 2 x 32 KB: both issued one stage ahead.
-//   FP8:  256 rows, 4 waves (2 x 2, wave tile 128 x 128, 256 accumulators), token rows 2 x 32 KB
-//         issued one stage ahead + weights 3 x 32 KB issued two stages ahead.
+//   FP8:  256 rows, 8 waves (4 x 2, wave tile 64 x 128, 128 accumulators, two waves per SIMD;
+//         weight fragments read in two halves), token rows 2 x 32 KB issued one stage ahead +
+//         weights 3 x 32 KB issued two stages ahead (320-row tiles would not fit the registers).
 template <bool FP8>
 struct PipeCfg {
   static constexpr int BM = FP8 ? 256 : 320;
-  static constexpr int WAVES = FP8 ? 4 : 8;
+  static constexpr int WAVES = 8;
   static constexpr int AST = 2, BST = FP8 ? 3 : 2;
   static constexpr int kLoadsA = BM / kPRowsPerLoad;    // wave loads per stage, token rows
   static constexpr int kLoadsB = kPBN / kPRowsPerLoad;  // ... and weight rows
@@ -232,6 +233,31 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
       }
       const unsigned char* sa = aring + (kt % C::AST) * C::kAStageBytes;
       const unsigned char* sb = bring + (kt % C::BST) * C::kBStageBytes;
+      if constexpr (FP8) {
+        // FP8 fragments are 8 registers: the token fragments first, then the weight fragments in
+        // two halves of 4, each followed by its MFMAs (two waves per SIMD fit without spills)
+        typename M::frag af[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          af[i] = M::read(sa + (wm + WMW * i) * 16 * kPRowBytes, frag_off[0]);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          typename M::frag bw[4];
+#pragma unroll
+          for (int nn = 0; nn < 4; ++nn) {
+            const int n = 4 * hb + nn;
+            const int grp = GATE_UP ? (n < 4 ? 4 * wn + n : 8 + 4 * wn + (n - 4)) : 8 * wn + n;
+            bw[nn] = M::read(sb + grp * 16 * kPRowBytes, frag_off[0]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int nn = 0; nn < 4; ++nn)
+              acc[i][4 * hb + nn] = M::mma(af[i], bw[nn], acc[i][4 * hb + nn]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int s = 0; s < M::kSteps; ++s) {
         typename M::frag bw[8], af[NV];
@@ -267,6 +293,15 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
       kloop(std::integral_constant<int, 4>{});
     else
       kloop(std::integral_constant<int, 2>{});
+  } else if constexpr (NVMAX == 4) {
+    if (nv > 3)
+      kloop(std::integral_constant<int, 4>{});
+    else if (nv > 2)
+      kloop(std::integral_constant<int, 3>{});
+    else if (nv > 1)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 1>{});
   } else {
     static_assert(NVMAX == 5, "loop bodies for 5 sub-tiles per wave");
     if (nv > 4)
