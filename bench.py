@@ -381,7 +381,7 @@ def main():
                            ROUTED.get(a.workload, (a.workload,))[0], a.cpu_tokens)
     sh = wl.shape
     line = {
-        "metric": "MoE-layer tokens/sec (d5120, 256 exp, top-8); % of roofline",
+        "metric": "MoE-layer tokens/sec (d5120, 256 exp, top-8) at T=32 and T=8192; % of roofline",
         "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": main_res["dtype"], "data": "synthetic",
