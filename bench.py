@@ -30,6 +30,8 @@ FLOP/B = T*K/E (bf16) or 2*T*K/E (FP8); below the ridge (bf16 2.5 PFLOP/s / 8 TB
 traffic: HBM bytes of that kernel from rocprofv3 --pmc runs (2.0 x FETCH_SIZE + WRITE_SIZE, the
 factor from a 1 GiB copy), stored in profiles/counters_<workload>.json with a hash of the kernel
 sources; null if the file is missing or the sources changed since.
+ceilings: measured context for the fractions (vendor-library calls, not the measured path): a 4 GiB
+device copy, an 8192^3 bf16 matmul and a dense batched bf16 GEMM of the prefill gate/up shape.
 cpu_baseline: the CPU oracle (float64 numpy) on a bounded sample of the same batch (routing of the
 whole batch + expert MLPs and combine for the first --cpu-tokens tokens), on the host's cores.
 """
@@ -70,6 +72,8 @@ def parse():
                    "dense_prefill,boundary_prefill",
                    help="comma list of extra workloads ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured HBM / GEMM ceilings (vendor-library context)")
     p.add_argument("--cpu-tokens", type=int, default=32)
     p.add_argument("--copy-probe-gib", type=float, default=0.0,
                    help="also run a plain device copy of this size (counter scaling reference)")
@@ -279,6 +283,44 @@ def measure_boundary(bm, synthgen, torch, weights, steps, warmup):
                                     "frac": alone_bytes / (alone * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
+def ceilings(torch):
+    """Measured ceilings on this GPU, context for the roofline fractions (vendor library calls, not
+    the measured path): HBM bandwidth of a 4 GiB device copy (read + write bytes); bf16 dense GEMM
+    rate of an 8192^3 matmul; and a batched bf16 GEMM of the prefill gate/up shape (256 experts x
+    256 rows x 5120 x 5120, dense, both operands contiguous)."""
+    def clock(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    res = {}
+    src = torch.empty(2 ** 30, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    t = clock(lambda: dst.copy_(src), 10)
+    res["hbm_copy_GBps"] = 2 * src.numel() * 4 / t / 1e9
+    del src, dst
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    t = clock(lambda: torch.mm(a, b), 10)
+    res["bf16_gemm_8192_TFLOPs"] = 2.0 * 8192 ** 3 / t / 1e12
+    del a, b
+    w = (torch.randn(256, 5120, 5120, device="cuda") * 0.02).to(torch.bfloat16)
+    xt = torch.randn(256, 5120, 256, device="cuda").to(torch.bfloat16)
+    o = torch.empty(256, 5120, 256, device="cuda", dtype=torch.bfloat16)
+    t = clock(lambda: torch.bmm(w, xt, out=o), 5)
+    res["bf16_batched_gemm_gate_up_shape_TFLOPs"] = 2.0 * 256 * 256 * 5120 * 5120 / t / 1e12
+    del w, xt, o
+    torch.cuda.empty_cache()
+    res["note"] = ("vendor-library rates on this GPU for context; the bench's kernels are the "
+                   "library's own HIP kernels")
+    return res
+
+
 def roofline(r, workload):
     g = r["gate_up"]
     if r["bound"] == "hbm":
@@ -373,6 +415,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceil = None
+    if not a.no_ceilings:
+        print("[bench] measuring HBM and GEMM ceilings", file=sys.stderr, flush=True)
+        ceil = ceilings(torch)
     cpu = None
     wl = synthgen.WORKLOADS[ROUTED.get(a.workload, (a.workload,))[0]]
     if not a.no_cpu_baseline:
@@ -392,6 +438,7 @@ def main():
                    "T": wl.T, "global_batch": wl.T, "parallelism": "single GPU"},
         "roofline": roofline(main_res, a.workload),
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "detail": main_res,
         "also": extra,
     }
