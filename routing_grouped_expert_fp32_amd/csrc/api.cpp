@@ -53,7 +53,8 @@ struct Layout {
   int bm = 0;
 };
 
-Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full) {
+// ybuf_parts > 1: room for the partial sums of a K-split down GEMM (dense layer)
+Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full, int ybuf_parts = 1) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -84,7 +85,7 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full) {
     L.sorted = take(sizeof(int32_t) * (size_t)TK);
     const size_t hel = c.w_dtype == BEAM_F32 ? 4 : 2;
     L.hbuf = take(hel * (size_t)TK * (size_t)c.d_ff);
-    L.ybuf = take(sizeof(float) * (size_t)TK * (size_t)c.hidden);
+    L.ybuf = take(sizeof(float) * (size_t)TK * (size_t)ybuf_parts * (size_t)c.hidden);
     if (c.w_dtype == BEAM_FP8_E4M3) {
       L.xq = take((size_t)T * (size_t)c.hidden);
       L.xs = take(sizeof(float) * (size_t)T);
@@ -148,6 +149,8 @@ bool any_alias(const std::vector<Range>& ins, const std::vector<Range>& outs) {
   return false;
 }
 
+int g_cus[kMaxDevices];   // compute units per device, cached by check_device
+
 beam_status_t check_device() {
   static int arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
   static std::mutex mu;
@@ -158,8 +161,16 @@ beam_status_t check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BEAM_ERR_DEVICE;
     arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev] = prop.multiProcessorCount;
   }
   return arch_ok[dev] == 1 ? BEAM_OK : BEAM_ERR_DEVICE;
+}
+
+// compute units of the current device (after a successful check_device)
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  return g_cus[dev] > 0 ? g_cus[dev] : 256;
 }
 
 // ---- stage timing ------------------------------------------------------------------------------
@@ -231,7 +242,7 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
                           const void* w_gate_up, const void* w_down,
                           const float* w_gate_up_scale, const float* w_down_scale, void* out,
                           int e_begin, int e_count, bool filter, hipStream_t st,
-                          const beam::BoundaryArgs* bnd = nullptr) {
+                          const beam::BoundaryArgs* bnd = nullptr, int ksplit = 1) {
   const beam::AlignTables at = align_tables(L, ws);
   float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
   const beam::Shape s = shape_of(c, T);
@@ -252,7 +263,7 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
       LAUNCH(4, beam::launch_gate_up(x, w_gate_up, hbuf, nullptr, nullptr, false, at, s,
                                      L.max_blocks, small, st));
       LAUNCH(6, beam::launch_down(hbuf, w_down, nullptr, nullptr, false, tw, ybuf, at, s,
-                                  L.max_blocks, small, st));
+                                  L.max_blocks, small, st, ksplit));
     } else {
       uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
       uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
@@ -265,7 +276,7 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
                                      L.max_blocks, small, st));
       LAUNCH(5, beam::launch_quant_rows_fp8(hbuf, T * c.topk, c.d_ff, hq, hs, st));
       LAUNCH(6, beam::launch_down(hq, w_down, hs, w_down_scale, true, tw, ybuf, at, s,
-                                  L.max_blocks, small, st));
+                                  L.max_blocks, small, st, ksplit));
     }
   }
   if (bnd) {   // combine fused into the post-MoE boundary
@@ -273,7 +284,9 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
                                     e_begin + e_count, nullptr, false, T, c.hidden, st));
     return BEAM_OK;
   }
-  LAUNCH(7, beam::launch_combine(ybuf, out, c.out_dtype == BEAM_BF16, s, filter ? ids : nullptr,
+  beam::Shape sc = s;   // a K-split down leaves ksplit partial rows per slot, summed in order
+  sc.K = s.K * ksplit;
+  LAUNCH(7, beam::launch_combine(ybuf, out, c.out_dtype == BEAM_BF16, sc, filter ? ids : nullptr,
                                  e_begin, e_begin + e_count, st));
   return BEAM_OK;
 }
@@ -608,9 +621,21 @@ beam_status_t check_dense(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t
   return BEAM_OK;
 }
 
+// Largest K split the dense down GEMM may take (tiled blocks; parts of at least 16 stages). The
+// workspace holds that many partial rows per token, so its size does not depend on the device.
+int dense_ksplit_max(const beam_moe_cfg& c, int64_t T) {
+  if (use_small_blocks(c, T)) return 1;
+  const int64_t k_stages = (int64_t)c.d_ff * dtype_bytes(c.w_dtype) / 128;
+  int m = 1;
+  for (int ks = 2; ks <= 4; ks *= 2)
+    if (k_stages % ks == 0 && k_stages / ks >= 16) m = ks;
+  return m;
+}
+
 size_t beam_dense_mlp_workspace_bytes(int32_t hidden, int32_t d_ff, int32_t w_dtype, int64_t T) {
   if (check_dense(hidden, d_ff, w_dtype, BEAM_F32, T) != BEAM_OK) return 0;
-  return make_layout(dense_cfg(hidden, d_ff, w_dtype, BEAM_F32), T, true).total;
+  const beam_moe_cfg c = dense_cfg(hidden, d_ff, w_dtype, BEAM_F32);
+  return make_layout(c, T, true, dense_ksplit_max(c, T)).total;
 }
 
 beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_up, const void* w_down,
@@ -632,7 +657,8 @@ beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_up, const
       (w_down_scale && !aligned16(w_down_scale)))
     return BEAM_ERR_ALIGN;
   const beam_moe_cfg c = dense_cfg(hidden, d_ff, w_dtype, out_dtype);
-  const Layout L = make_layout(c, T, true);
+  const int ks_max = dense_ksplit_max(c, T);
+  const Layout L = make_layout(c, T, true, ks_max);
   if (L.max_blocks > 65535) return BEAM_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
   const size_t H = hidden, F = d_ff, wb = dtype_bytes(w_dtype);
@@ -652,8 +678,16 @@ beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_up, const
   int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
   float* tw = reinterpret_cast<float*>(ws + L.w);
   if (beam::launch_fill_dense_routes(ids, tw, T, st) != hipSuccess) return BEAM_ERR_LAUNCH;
+  // one expert: the tiled down GEMM has ceil(T / BM) x (hidden / 256) workgroups, few enough at
+  // prefill sizes that a K split evens out the last round
+  int ks = 1;
+  if (ks_max > 1) {
+    const int64_t tiles = ceil_div(T, (int64_t)L.bm) * (hidden / beam::kPipeDownCols);
+    ks = std::min(ks_max, beam::down_ksplit(tiles, (int64_t)d_ff * dtype_bytes(w_dtype) / 128,
+                                            device_cus()));
+  }
   return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
-                     out, 0, 1, false, st);
+                     out, 0, 1, false, st, nullptr, ks);
 }
 
 beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols, uint8_t* codes,

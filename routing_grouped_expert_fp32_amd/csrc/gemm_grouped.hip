@@ -14,6 +14,8 @@
 //     grouped_small_ks_kernel (K split across the waves of a workgroup) where the shape allows.
 //   large blocks (320 rows bf16, 256 rows FP8; prefill): grouped_pipe_kernel, LDS rings fed by
 //     direct loads.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm_pipe.h"
 #include "gemm_small.h"
@@ -27,7 +29,7 @@ template <bool GATE_UP, bool FP8>
 static void launch_one(const void* a, const void* w, const float* topk_w, void* out,
                        const float* a_scale, const float* w_scale, const AlignTables& at,
                        int Kd, int Nout, int topk, int64_t max_blocks, bool small,
-                       hipStream_t st) {
+                       hipStream_t st, int ksplit = 1) {
   const auto* A = reinterpret_cast<const unsigned char*>(a);
   const auto* W = reinterpret_cast<const unsigned char*>(w);
   if (small) {
@@ -48,10 +50,10 @@ static void launch_one(const void* a, const void* w, const float* topk_w, void* 
     }
   } else {
     const int n_ctiles = GATE_UP ? Nout / 128 : Nout / 256;
-    const int64_t wgs = 8 * ceil_div(max_blocks * n_ctiles, 8);
+    const int64_t wgs = 8 * ceil_div(max_blocks * n_ctiles * ksplit, 8);
     hipLaunchKernelGGL((grouped_pipe_kernel<GATE_UP, FP8>), dim3((unsigned)wgs),
                        dim3(64 * PipeCfg<FP8>::WAVES), 0, st, A, W, topk_w, out, at, Kd, Nout, topk,
-                       n_ctiles, a_scale, w_scale);
+                       n_ctiles, a_scale, w_scale, ksplit);
   }
 }
 
@@ -70,15 +72,39 @@ hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const
 
 hipError_t launch_down(const void* h, const void* w_dn, const float* h_scale, const float* w_scale,
                        bool fp8, const float* topk_w, float* ybuf, const AlignTables& at,
-                       const Shape& s, int64_t max_blocks, bool small, hipStream_t st) {
+                       const Shape& s, int64_t max_blocks, bool small, hipStream_t st,
+                       int ksplit) {
   if (s.T == 0) return hipSuccess;
+  if (ksplit != 1 && (small || (s.F * (fp8 ? 1 : 2) / kPRowBytes) % ksplit != 0))
+    return hipErrorInvalidValue;
   if (fp8)
     launch_one<false, true>(h, w_dn, topk_w, ybuf, h_scale, w_scale, at, s.F, s.H, s.K,
-                            max_blocks, small, st);
+                            max_blocks, small, st, ksplit);
   else
     launch_one<false, false>(h, w_dn, topk_w, ybuf, nullptr, nullptr, at, s.F, s.H, s.K,
-                             max_blocks, small, st);
+                             max_blocks, small, st, ksplit);
   return hipGetLastError();
+}
+
+int down_ksplit(int64_t tiles, int64_t k_stages, int n_cu) {
+  // Workgroups run one per CU, dealt to the 8 XCDs in contiguous ranges; a grid whose last round
+  // is nearly empty leaves most CUs idle for one workgroup's time. Choose the K split (1, 2 or 4)
+  // with the fewest rounds per unit of work, charging each extra part a little for its partial-sum
+  // traffic; parts keep at least 16 stages.
+  const int64_t cu_per_xcd = std::max(1, n_cu / 8);
+  int best = 1;
+  double best_cost = 1e30;
+  for (int ks = 1; ks <= 4; ks *= 2) {
+    if (k_stages % ks != 0 || k_stages / ks < 16) continue;
+    const int64_t per_xcd = ceil_div(tiles * ks, 8);
+    const double rounds = (double)ceil_div(per_xcd, cu_per_xcd);
+    const double cost = rounds / ks + 0.05 * (ks - 1);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = ks;
+    }
+  }
+  return best;
 }
 
 }  // namespace beam

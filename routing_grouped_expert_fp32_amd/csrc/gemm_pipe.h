@@ -119,7 +119,8 @@ template <bool GATE_UP, bool FP8>
 __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
     const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
-    int topk, int n_ctiles, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
+    int topk, int n_ctiles, const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+    int ksplit) {
   using M = PipeMath<FP8>;
   using C = PipeCfg<FP8>;
   constexpr int WAVES = C::WAVES;
@@ -129,12 +130,16 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // ---- tile assignment (XCD-aware) ----
   const int L = blockIdx.x;
   const int xcd = L & 7, local = L >> 3;
-  const int total = at.n_blocks[0] * n_ctiles;
+  const int tiles = at.n_blocks[0] * n_ctiles;
+  const int total = tiles * ksplit;
   const int per = (total + 7) >> 3;
   if (local >= per) return;
   const int v = xcd * per + local;
   if (v >= total) return;
-  const int b = v / n_ctiles, j = v % n_ctiles;
+  // K split (down only): part ksp of ksplit covers stages [ksp * nk, (ksp + 1) * nk) of the row
+  // and writes its partial sums to output row slot * ksplit + ksp
+  const int ksp = v / tiles, vt = v - ksp * tiles;
+  const int b = vt / n_ctiles, j = vt % n_ctiles;
   const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
 
   // waves: WAVES / 2 wave rows x 2 wave columns; wave row wm takes the 16-row sub-tiles
@@ -143,6 +148,8 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
+  const int nk = (int)(row_bytes / kPRowBytes) / ksplit;   // stages of this part
+  const int64_t kbeg = (int64_t)ksp * nk * kPRowBytes;
 
   // ---- direct-load sources. Wave w issues token-row loads a = w*LA .. and weight-row loads
   // q = w*LB ..; load a covers block rows [8a, 8a+8): lane -> row 8a + lane/8, chunk slot lane%8,
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
     if (rr >= rows) rr = rows - 1;                      // padding rows re-read a valid row
     const int64_t arow =
         GATE_UP ? (int64_t)(at.sorted_slot[row0 + rr] / topk) : (int64_t)(row0 + rr);
-    asrc[q] = A + arow * row_bytes + gchunk * 16;
+    asrc[q] = A + arow * row_bytes + kbeg + gchunk * 16;
   }
   // weight tile row br = (wave*LB + q)*8 + lrow; gate/up tiles: rows [0,128) gate, [128,256) up.
   // A wave's LB loads cover 8 LB consecutive tile rows, all in one half.
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
     wrow0 = (int64_t)e * 2 * Nout + (br0 < 128 ? 128 * j + br0 : Nout + 128 * j + (br0 - 128));
   else
     wrow0 = (int64_t)e * Nout + 256 * j + br0;
-  const unsigned char* bsrc = W + wrow0 * row_bytes + gchunk * 16;
+  const unsigned char* bsrc = W + wrow0 * row_bytes + kbeg + gchunk * 16;
   const int64_t bstep = (int64_t)kPRowsPerLoad * row_bytes;   // bytes between consecutive loads
 
   auto issue_a = [&](int stage) {
@@ -201,7 +208,6 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // entering iteration kt the wave's queue ends with B(kt), A(kt), B(kt+1): all but the youngest
   // LB loads must have completed. BST == 2: prologue A(0), B(0); iteration kt issues A(kt+1),
   // B(kt+1) after its barrier, so entering it everything issued must have completed.
-  const int nk = (int)(row_bytes / kPRowBytes);
   issue_a(0);
   issue_b(0);
   if constexpr (C::BST == 3)
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
           const int col = 256 * j + 128 * wn + 16 * n + r;
           float y = acc[i][n][q];
           if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
-          reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = wgt * y;
+          reinterpret_cast<float*>(out)[((int64_t)slot * ksplit + ksp) * Nout + col] = wgt * y;
         }
       }
     }

@@ -34,12 +34,16 @@ def _oracle(d, w_dtype, toks):
     return experts.expert_mlp(xr, ex, w_dtype)
 
 
-@pytest.mark.parametrize("w_dtype,T", [("bf16", 3), ("bf16", 100), ("bf16", 600), ("fp8", 5),
-                                       ("fp8", 600)])
-def test_small_dense_all_tokens(w_dtype, T):
-    """hidden 512, d_ff 1024: decode-sized (16-row blocks) and tiled (256-row blocks) paths."""
-    _say("dense small", w_dtype, T)
-    d = synthgen.make_dense(T, 512, 1024, w_dtype, device="cuda", sigma_w=0.05)
+@pytest.mark.parametrize("w_dtype,T,d_ff", [("bf16", 3, 1024), ("bf16", 100, 1024),
+                                            ("bf16", 600, 1024), ("fp8", 5, 1024),
+                                            ("fp8", 600, 1024), ("bf16", 600, 4096),
+                                            ("bf16", 1000, 4096)])
+def test_small_dense_all_tokens(w_dtype, T, d_ff):
+    """hidden 512: decode-sized (16-row blocks) and tiled paths; with d_ff 4096 the few tiled
+    workgroups make the bf16 down GEMM split K into 4 parts of 16 stages (FP8 splits are covered
+    at Beam's dense shape below)."""
+    _say("dense small", w_dtype, T, d_ff)
+    d = synthgen.make_dense(T, 512, d_ff, w_dtype, device="cuda", sigma_w=0.05)
     out = _run(d, w_dtype).cpu().numpy()
     ref = _oracle(d, w_dtype, np.arange(T))
     err, rms = parity.rel_err(out, ref)
@@ -86,3 +90,24 @@ def test_beam_dense_decode_all_tokens(beam_dense):
     err, rms = parity.rel_err(out, ref)
     _say("Beam dense T=32 max|err|/rms", err)
     assert err <= parity.TOL["bf16"]
+
+
+def test_beam_dense_fp8_sampled():
+    """Beam's dense layer with FP8 weights at T = 8192 (the down GEMM splits K into 4 parts),
+    sampled tokens against the oracle's FP8 contract; and at T = 32 every token."""
+    _say("generating Beam dense layer (5120 x 20480, FP8) on cuda:0")
+    d = synthgen.make_dense(8192, w_dtype="fp8", device="cuda")
+    torch.cuda.synchronize()
+    out = _run(d, "fp8")
+    toks = np.array([0, 1, 777, 4095, 6000, 8191])
+    ref = _oracle(d, "fp8", toks)
+    err, rms = parity.rel_err(out[torch.from_numpy(toks).cuda()].cpu().numpy(), ref)
+    _say("Beam dense FP8 T=8192 sampled max|err|/rms", err)
+    assert err <= parity.TOL["fp8"]
+    d32 = dict(d)
+    d32["x"] = d["x"][:32].contiguous()
+    d32["T"] = 32
+    out = _run(d32, "fp8").cpu().numpy()
+    err, rms = parity.rel_err(out, _oracle(d32, "fp8", np.arange(32)))
+    _say("Beam dense FP8 T=32 max|err|/rms", err)
+    assert err <= parity.TOL["fp8"]
