@@ -76,3 +76,25 @@ def test_timing_stage_mask():
     st = bm.timing_collect()
     for k in ("router_logits", "router_select", "moe_align", "gate_up", "down", "combine"):
         assert st[k][1] == 1, (k, st)
+
+
+def test_two_streams_with_their_own_workspaces():
+    """Calls on two streams at once, each with its own workspace, give the results of serial calls
+    (the library keeps no state between calls besides the timing records)."""
+    run_a, out_a, ids_a = _case("bf16", 700)
+    run_b, out_b, ids_b = _case("fp8", 40)
+    run_a()
+    run_b()
+    torch.cuda.synchronize()
+    ref_a, ref_b = out_a.clone(), out_b.clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for i in range(3):
+        out_a.fill_(float("nan"))
+        out_b.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            run_a(s1)
+        with torch.cuda.stream(s2):
+            run_b(s2)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, ref_a) and torch.equal(out_b, ref_b), f"round {i}"
