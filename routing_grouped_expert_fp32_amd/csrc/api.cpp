@@ -35,7 +35,7 @@ size_t dtype_bytes(int32_t dt) {
 }
 
 // Block rows of moe_align for this call: small decode-like batches stream weights through 16-row
-// blocks; larger ones use the LDS-tiled kernels (320-row blocks bf16, 256-row FP8). FP32 experts use
+// blocks; larger ones use the LDS-tiled kernels (320-row blocks, bf16 and FP8). FP32 experts use
 // 16-row blocks.
 bool use_small_blocks(const beam_moe_cfg& c, int64_t T) {
   return c.w_dtype == BEAM_F32 || T * c.topk <= 4 * (int64_t)c.n_experts;

@@ -12,7 +12,7 @@
 // bound on the block count; blocks past the device-side count exit at once (no host readback).
 //   small blocks (<= 16 rows, decode): grouped_small_kernel, weights streamed into registers;
 //     grouped_small_ks_kernel (K split across the waves of a workgroup) where the shape allows.
-//   large blocks (320 rows bf16, 256 rows FP8; prefill): grouped_pipe_kernel, LDS rings fed by
+//   large blocks (320 rows; prefill): grouped_pipe_kernel, LDS rings fed by
 //     direct loads.
 #include <algorithm>
 

@@ -2,21 +2,19 @@
 //
 // Used by the gate/up (fused SwiGLU epilogue) and down (weighted epilogue) steps when experts carry
 // many rows (prefill-sized batches). Design:
-//   * WG tile: BM rows of one expert (bf16 320, FP8 256) x 256 weight columns (gate/up: 128 gate
-//     columns and the 128 matching up columns), 8 waves in a 4 x 2 grid, two per SIMD, so one
-//     wave's barrier and LDS waits overlap the other's MFMAs. Wave tile 80 x 128 (bf16, 160 fp32
-//     accumulators per lane) or 64 x 128 (FP8, 128 accumulators; its 8-register weight fragments
-//     are read in two halves). bf16 uses v_mfma_f32_16x16x32_bf16, FP8 the 16x16x128 f8f6f4 MFMA
-//     with unit block scales (operands OCP E4M3FN).
+//   * WG tile: 320 rows of one expert x 256 weight columns (gate/up: 128 gate columns and the 128
+//     matching up columns), 8 waves in a 4 x 2 grid, two per SIMD, so one wave's barrier and LDS
+//     waits overlap the other's MFMAs. Wave tile 80 x 128 (160 fp32 accumulators per lane). bf16
+//     uses v_mfma_f32_16x16x32_bf16; FP8 the 16x16x128 f8f6f4 MFMA with unit block scales
+//     (operands OCP E4M3FN), its 8-register weight fragments read in two halves.
 //   * Each stage carries 128 bytes of every row (64 bf16 or 128 FP8 values). Global -> LDS with
 //     global_load_lds_dwordx4: one wave instruction lands 1 KB = 8 rows x 128 B (whole cache
 //     lines) contiguously in LDS; each lane fetches the 16-byte chunk that belongs at its LDS slot.
 //     Chunk c of row r is stored at chunk position c ^ (r & 7), so the 16 rows a fragment read
 //     touches fall on distinct banks.
-//   * Separate LDS rings: token rows (L2-resident, short latency) 2 stages, issued one stage
-//     ahead; weights (streamed from HBM) 2 stages issued one stage ahead (bf16: 2 x 40 KB + 2 x
-//     32 KB) or 3 stages issued two stages ahead (FP8: 2 x 32 KB + 3 x 32 KB = 160 KB). Each wave
-//     waits (s_waitcnt vmcnt) only for its own loads of the stage it reads.
+//   * Separate LDS rings: token rows (L2-resident, short latency) 2 x 40 KB and weights (streamed
+//     from HBM) 2 x 32 KB, both issued one stage ahead; each stage begins with a wait for the
+//     wave's own loads and a workgroup barrier.
 //   * Row sub-tiles are dealt to the wave rows in turn (wave row wm of 4 takes 16-row sub-tiles
 //     wm, wm+4, ...); a wave runs one of four K-loop bodies, chosen by how many of its sub-tiles
 //     hold rows, so a partly filled block costs about its rows.
@@ -40,18 +38,15 @@ constexpr int kPChunks = kPRowBytes / 16;       // 16-byte chunks per row per st
 constexpr int kPRowsPerLoad = 64 / kPChunks;    // rows covered by one 1 KB wave load
 static_assert(kPChunks == 8, "swizzle below is defined for 128-byte rows");
 
-// Per element type: block rows (BM), waves per workgroup, LDS ring depths.
-//   bf16: 320 rows (every expert of a 256-rows-per-expert batch fits one block, so its weights
-//         stream once), 8 waves (4 x 2, wave tile 80 x 128, 160 accumulators, two waves per SIMD),
-//         token rows 2 x 40 KB + weights 2 x 32 KB: both issued one stage ahead.
-//   FP8:  256 rows, 8 waves (4 x 2, wave tile 64 x 128, 128 accumulators, two waves per SIMD;
-//         weight fragments read in two halves), token rows 2 x 32 KB issued one stage ahead +
-//         weights 3 x 32 KB issued two stages ahead (320-row tiles would not fit the registers).
+// Block shape, both element types: 320 rows (every expert of a 256-rows-per-expert batch fits one
+// block, so its weights stream once and the grid has one workgroup per expert and column tile),
+// 8 waves (4 x 2, wave tile 80 x 128, 160 accumulators, two waves per SIMD), token rows 2 x 40 KB +
+// weights 2 x 32 KB, both issued one stage ahead (144 KB of LDS).
 template <bool FP8>
 struct PipeCfg {
-  static constexpr int BM = FP8 ? 256 : 320;
+  static constexpr int BM = 320;
   static constexpr int WAVES = 8;
-  static constexpr int AST = 2, BST = FP8 ? 3 : 2;
+  static constexpr int AST = 2, BST = 2;
   static constexpr int kLoadsA = BM / kPRowsPerLoad;    // wave loads per stage, token rows
   static constexpr int kLoadsB = kPBN / kPRowsPerLoad;  // ... and weight rows
   static constexpr int kAStageBytes = BM * kPRowBytes;
@@ -59,7 +54,7 @@ struct PipeCfg {
   static constexpr int kLdsBytes = AST * kAStageBytes + BST * kBStageBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(kLoadsA % WAVES == 0 && kLoadsB % WAVES == 0, "loads split evenly over waves");
-  static_assert((kLoadsA + kLoadsB) / WAVES * BST < 64, "vmcnt range");
+  static_assert((kLoadsA + kLoadsB) / WAVES < 64, "vmcnt range");
 };
 
 // cache-policy operand of the direct loads: non-temporal for the weight stream (a weight tile is
@@ -201,17 +196,11 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Issue order: prologue A(0), B(0), B(1); iteration kt issues A(kt+1), B(kt+2). Entering
-  // iteration kt the wave's queue ends with B(kt), A(kt), B(kt+1): all but the youngest LB loads
-  // must have completed.
-  // Issue order. BST == 3: prologue A(0), B(0), B(1); iteration kt issues A(kt+1), B(kt+2);
-  // entering iteration kt the wave's queue ends with B(kt), A(kt), B(kt+1): all but the youngest
-  // LB loads must have completed. BST == 2: prologue A(0), B(0); iteration kt issues A(kt+1),
-  // B(kt+1) after its barrier, so entering it everything issued must have completed.
+  // Issue order: prologue A(0), B(0); iteration kt waits for everything it issued, passes the
+  // barrier (every wave's loads of stage kt have landed and every wave is done reading stage
+  // kt - 1, whose slots are reused), then issues A(kt+1), B(kt+1) and computes stage kt.
   issue_a(0);
   issue_b(0);
-  if constexpr (C::BST == 3)
-    if (1 < nk) issue_b(1);
 
   // fragment byte offsets of this lane inside a 16-row group, per MFMA step of a stage:
   // row r = lane % 16, chunk M::chunk(step, lane / 16, half) (swizzled)
@@ -226,26 +215,16 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   auto kloop = [&](auto nv_tag) {
     constexpr int NV = decltype(nv_tag)::value;
     for (int kt = 0; kt < nk; ++kt) {
-      if (C::BST == 3 && kt + 1 < nk)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LB));   // B(kt+1) may stay in flight
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_ring_barrier();
       if (kt + 1 < nk) issue_a(kt + 1);
-      if constexpr (C::BST == 3) {
-        if (kt + 2 < nk) issue_b(kt + 2);
-      } else {
-        if (kt + 1 < nk) issue_b(kt + 1);
-      }
+      if (kt + 1 < nk) issue_b(kt + 1);
       const unsigned char* sa = aring + (kt % C::AST) * C::kAStageBytes;
       const unsigned char* sb = bring + (kt % C::BST) * C::kBStageBytes;
       if constexpr (FP8) {
-        // FP8 fragments are 8 registers: the token fragments first, then the weight fragments in
-        // two halves of 4, each followed by its MFMAs (two waves per SIMD fit without spills)
-        typename M::frag af[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-          af[i] = M::read(sa + (wm + WMW * i) * 16 * kPRowBytes, frag_off[0]);
+        // FP8 fragments are 8 registers: the weight fragments are read in two halves of 4, and
+        // within a half each token fragment is read just before its 4 MFMAs (every token fragment
+        // is read twice per stage), so 160 accumulators and two waves per SIMD fit without spills
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           typename M::frag bw[4];
@@ -257,10 +236,12 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < NV; ++i)
+          for (int i = 0; i < NV; ++i) {
+            const typename M::frag af = M::read(sa + (wm + WMW * i) * 16 * kPRowBytes, frag_off[0]);
 #pragma unroll
             for (int nn = 0; nn < 4; ++nn)
-              acc[i][4 * hb + nn] = M::mma(af[i], bw[nn], acc[i][4 * hb + nn]);
+              acc[i][4 * hb + nn] = M::mma(af, bw[nn], acc[i][4 * hb + nn]);
+          }
         }
         continue;
       }
@@ -290,35 +271,15 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // valid sub-tiles of this wave: mt = wm + WMW i < ceil(rows / 16); four loop bodies
   const int nsub = (rows + 15) >> 4;
   const int nv = nsub > wm ? min(NVMAX, (nsub - wm + WMW - 1) / WMW) : 0;
-  if constexpr (NVMAX == 8) {
-    if (nv > 6)
-      kloop(std::integral_constant<int, 8>{});
-    else if (nv > 4)
-      kloop(std::integral_constant<int, 6>{});
-    else if (nv > 2)
-      kloop(std::integral_constant<int, 4>{});
-    else
-      kloop(std::integral_constant<int, 2>{});
-  } else if constexpr (NVMAX == 4) {
-    if (nv > 3)
-      kloop(std::integral_constant<int, 4>{});
-    else if (nv > 2)
-      kloop(std::integral_constant<int, 3>{});
-    else if (nv > 1)
-      kloop(std::integral_constant<int, 2>{});
-    else
-      kloop(std::integral_constant<int, 1>{});
-  } else {
-    static_assert(NVMAX == 5, "loop bodies for 5 sub-tiles per wave");
-    if (nv > 4)
-      kloop(std::integral_constant<int, 5>{});
-    else if (nv > 3)
-      kloop(std::integral_constant<int, 4>{});
-    else if (nv > 2)
-      kloop(std::integral_constant<int, 3>{});
-    else
-      kloop(std::integral_constant<int, 2>{});
-  }
+  static_assert(NVMAX == 5, "loop bodies for 5 sub-tiles per wave");
+  if (nv > 4)
+    kloop(std::integral_constant<int, 5>{});
+  else if (nv > 3)
+    kloop(std::integral_constant<int, 4>{});
+  else if (nv > 2)
+    kloop(std::integral_constant<int, 3>{});
+  else
+    kloop(std::integral_constant<int, 2>{});
 
   // ---- epilogue ----
 #pragma unroll
