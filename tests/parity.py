@@ -74,9 +74,10 @@ def rel_err(out, ref):
 
 
 def check_outputs(out_gpu, x, ids_gpu, rres: router.RouteResult, scale, get_expert, contract,
-                  tokens):
+                  tokens, arrays=False):
     """Output parity on `tokens` (indices into the full batch). Tokens whose id set matches use the
-    oracle's routing; near-tie tokens use the GPU's ids with oracle weights for them."""
+    oracle's routing; near-tie tokens use the GPU's ids with oracle weights for them. Returns
+    (max|err|/rms, rms), and with arrays=True also the GPU and oracle outputs compared."""
     tokens = np.asarray(tokens)
     ids_gpu = np.asarray(ids_gpu, dtype=np.int64)[tokens]
     use_ids = rres.ids[tokens].copy()
@@ -89,4 +90,6 @@ def check_outputs(out_gpu, x, ids_gpu, rres: router.RouteResult, scale, get_expe
     got = np.asarray(out_gpu, dtype=np.float64)
     if got.shape[0] != len(tokens):
         got = got[tokens]
+    if arrays:
+        return rel_err(got, ref) + (got, ref)
     return rel_err(got, ref)
