@@ -10,7 +10,9 @@ gate/up GEMM, down GEMM, combine), inputs already resident in HBM. The timed reg
 torch.cuda.synchronize() on both sides; inside it the library records HIP events on the call's
 stream around the gate/up GEMM only (the roofline kernel), which gives that kernel's average
 duration without event records between the other kernels; stages_ms comes from a second,
-instrumented pass of the same steps with every stage recorded. Prints ONE JSON line; the
+instrumented pass of the same steps with every stage recorded, and its step_ms_p10_median_p90 from a
+third pass with an event pair around every call. route_only_ms times beam_moe_route on its own.
+Prints ONE JSON line; the
 headline `value` is the --workload (decode, T=32, the configuration the metric is quoted on), the
 other workloads are reported under "also". skew is the T=32768 batch whose correction bias puts
 40% of the slots on 16 hot experts (about 6.5K rows each, MFMA-bound). routed_prefill / routed_decode time
@@ -33,7 +35,8 @@ sources; null if the file is missing or the sources changed since.
 ceilings: measured context for the fractions (vendor-library calls, not the measured path): a 4 GiB
 device copy, an 8192^3 bf16 matmul and a dense batched bf16 GEMM of the prefill gate/up shape.
 cpu_baseline: the CPU oracle (float64 numpy) on a bounded sample of the same batch (routing of the
-whole batch + expert MLPs and combine for the first --cpu-tokens tokens), on the host's cores.
+whole batch + expert MLPs and combine for the first --cpu-tokens tokens), on the host's cores;
+one_core: the same on one thread, experts of an eighth of the tokens.
 """
 from __future__ import annotations
 
@@ -124,6 +127,17 @@ def timed_steps(bm, torch, step, steps, warmup, stage):
     torch.cuda.synchronize()
     bm.timing_enable(False)
     stages = {k: (v[0] / v[1] if v[1] else None) for k, v in bm.timing_collect().items()}
+    # per-step spread: a third pass with an event pair around every call on the calling stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]  # noqa: E731
+    stages["step_ms_p10_median_p90"] = [q(0.1), q(0.5), q(0.9)]
     return elapsed * 1e3 / steps, tot / max(cnt, 1), stages
 
 
@@ -169,6 +183,23 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
                               stream=stream, **local)
 
     ms, gu_ms, stages_ms = timed_steps(bm, torch, step, steps, warmup, "gate_up")
+    route_ms = None
+    if not routed:   # beam_moe_route on its own (router logits + selection)
+        rws = torch.empty(max(bm.route_workspace_bytes(cfg, T), 16), dtype=torch.uint8,
+                          device="cuda")
+        rid = torch.empty((T, sh.topk), dtype=torch.int32, device="cuda")
+        rw = torch.empty((T, sh.topk), dtype=torch.float32, device="cuda")
+        rstep = lambda: bm.route(d["x"], W["w_router"], d["bias"], cfg, topk_ids=rid,  # noqa
+                                 topk_w=rw, workspace=rws, stream=stream)
+        for _ in range(warmup):
+            rstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            rstep()
+        torch.cuda.synchronize()
+        route_ms = (time.perf_counter() - t0) * 1e3 / steps
+        del rws
     u = torch.unique(ids)
     if routed:
         u = u[(u >= routed[1]) & (u < routed[2])]
@@ -195,6 +226,7 @@ def measure(bm, synthgen, torch, name, weights, steps, warmup):
         "layer_frac_of_mfma_peak": layer_flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[dt],
         "distinct_experts": distinct,
         "stages_ms": stages_ms,
+        "route_only_ms": route_ms,
         "gate_up": {"ms": gu_ms, "bytes": gu_bytes, "flops": gu_flops,
                     "GBps": gu_bytes / (gu_ms * 1e-3) / 1e9,
                     "TFLOPs": gu_flops / (gu_ms * 1e-3) / 1e12},
@@ -369,11 +401,32 @@ def cpu_baseline(torch, synthgen, d, W, wl_name, n_tok):
     t_exp = time.perf_counter() - t1
     # per-token cost of the whole block: routing amortised over the batch + experts per token
     per_tok = t_route / wl.T + t_exp / n_tok
-    return {"value": 1.0 / per_tok, "unit": "tokens/s",
-            "cores": int(max(blas, torch.get_num_threads())), "kind": "oracle",
-            "sample": f"{wl_name}: routing of all {wl.T} tokens ({t_route:.2f} s) + expert MLPs and "
-                      f"combine of {n_tok} tokens / {n_tok * sh.topk} expert calls ({t_exp:.2f} s), "
-                      f"float64 numpy"}
+    res = {"value": 1.0 / per_tok, "unit": "tokens/s",
+           "cores": int(max(blas, torch.get_num_threads())), "kind": "oracle",
+           "sample": f"{wl_name}: routing of all {wl.T} tokens ({t_route:.2f} s) + expert MLPs and "
+                     f"combine of {n_tok} tokens / {n_tok * sh.topk} expert calls ({t_exp:.2f} s), "
+                     f"float64 numpy"}
+    # the same on one core, on a smaller sample (routing of all tokens, experts of n1 tokens)
+    try:
+        from threadpoolctl import threadpool_limits
+        n1 = max(1, n_tok // 8)
+        nt = torch.get_num_threads()
+        torch.set_num_threads(1)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            r1 = router.route(x_h, wr_h, b_h, sh.n_groups, sh.topk_groups, sh.topk,
+                              sh.routed_scale)
+            t_route1 = time.perf_counter() - t0
+            t1 = time.perf_counter()
+            experts.forward_expert_major(x_h[:n1], r1.ids[:n1], r1.weights[:n1], get, "bf16")
+            t_exp1 = time.perf_counter() - t1
+        torch.set_num_threads(nt)
+        res["one_core"] = {"value": 1.0 / (t_route1 / wl.T + t_exp1 / n1), "unit": "tokens/s",
+                           "sample": f"routing of all {wl.T} tokens ({t_route1:.2f} s) + experts "
+                                     f"of {n1} tokens ({t_exp1:.2f} s), 1 thread"}
+    except ImportError:
+        res["one_core"] = None
+    return res
 
 
 def main():
