@@ -432,8 +432,10 @@ def cpu_baseline(torch, synthgen, d, W, wl_name, n_tok):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this build has no "
-              "multi-GPU path; see DESIGN.md for how the block would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the library has no "
+              "multi-GPU path. Across GPUs the block would shard by experts (one group of 32 per "
+              "GPU, an all-to-all dispatch and combine around beam_moe_forward_routed).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import routing_grouped_expert_fp32_amd as bm

@@ -79,7 +79,7 @@ enum { BEAM_F32 = 0, BEAM_BF16 = 1, BEAM_FP8_E4M3 = 2 };
  *                weights). BEAM_F32 experts require x_dtype BEAM_F32 and compute without any rounding
  *                point; BEAM_BF16 / BEAM_FP8_E4M3 experts require x_dtype BEAM_BF16.
  *   out_dtype    BEAM_F32 (graded output) or BEAM_BF16 (round-to-nearest-even copy)
- * Limits of this build: H % 256 == 0, F % 256 == 0, E <= 256, E % 16 == 0 and (E <= 64 or
+ * Limits of this library version: H % 256 == 0, F % 256 == 0, E <= 256, E % 16 == 0 and (E <= 64 or
  * E % 64 == 0), K <= 16, G <= 64, H * F < 2^31, T * K < 2^31. */
 typedef struct beam_moe_cfg {
   int32_t hidden;

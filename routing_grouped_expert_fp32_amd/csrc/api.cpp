@@ -111,7 +111,7 @@ beam_status_t check_cfg(const beam_moe_cfg* c, bool experts) {
   const bool od = c->out_dtype == BEAM_F32 || c->out_dtype == BEAM_BF16;
   if (!xd || !wd || !od) return BEAM_ERR_DTYPE;
   if ((c->x_dtype == BEAM_F32) != (c->w_dtype == BEAM_F32)) return BEAM_ERR_DTYPE;
-  // limits of this build
+  // limits of this library version
   if (c->hidden % 256 != 0 || c->n_experts > 256 || c->n_experts % 16 != 0 ||
       (c->n_experts > 64 && c->n_experts % 64 != 0) || c->n_groups > 64 || c->topk > 16)
     return BEAM_ERR_UNSUPPORTED;
@@ -342,7 +342,7 @@ const char* beam_status_string(beam_status_t s) {
     case BEAM_ERR_ALIGN: return "pointer not 16-byte aligned";
     case BEAM_ERR_SHAPE: return "inconsistent shape";
     case BEAM_ERR_DTYPE: return "unsupported dtype combination";
-    case BEAM_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case BEAM_ERR_UNSUPPORTED: return "shape or dtype not supported by this library version";
     case BEAM_ERR_WORKSPACE: return "workspace missing or too small";
     case BEAM_ERR_ALIAS: return "output overlaps another buffer";
     case BEAM_ERR_LAUNCH: return "kernel launch failed";
