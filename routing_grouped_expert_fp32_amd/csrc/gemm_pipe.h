@@ -20,8 +20,8 @@
 //     hold rows, so a partly filled block costs about its rows.
 //   * Tile order is XCD-aware: workgroup L runs on XCD L % 8; the (block, column-tile) space is cut
 //     into 8 contiguous ranges, one per XCD, walked column-tile fastest, so the workgroups sharing
-//     a block's token rows — and the blocks of one expert sharing weight tiles — run together on
-//     one XCD's L2.
+//     a block's token rows run together on one XCD's L2 (and consecutive blocks of one expert run
+//     on the same XCD).
 // Epilogues: gate/up  h = bf16( silu(bf16(g)) * bf16(u) ), g/u dequantised first for FP8
 //            (acc * token scale * output-channel scale); down  Y[slot] = topk_w[slot] * y (FP32),
 //            y = acc (* row scale * output-channel scale for FP8).
