@@ -140,7 +140,9 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // waves: WAVES / 2 wave rows x 2 wave columns; wave row wm takes the 16-row sub-tiles
   // wm, wm + WMW, ... (at most NVMAX of them), wave column wn half of the weight columns
   constexpr int WMW = WAVES / 2, NVMAX = (C::BM / 16) / WMW;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform, so the LDS destinations of the direct loads are scalar (no per-load readfirstlane)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
   const int nk = (int)(row_bytes / kPRowBytes) / ksplit;   // stages of this part
