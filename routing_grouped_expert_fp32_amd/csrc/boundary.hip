@@ -17,6 +17,8 @@
 // One workgroup of 256 threads per token; each thread keeps its chunks of 4 elements in registers
 // between the two reductions. Sums of squares: per-thread partials, a fixed xor butterfly per wave,
 // then the four wave sums in wave order (deterministic).
+#include <type_traits>
+
 #include "common.h"
 
 namespace beam {
@@ -36,7 +38,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 __device__ __forceinline__ float bf16r(float v) { return bf16_round(v); }
 
-template <bool SLOTS>
+// MAXCH: 4-float chunks per thread the registers hold (hidden <= MAXCH * 1024); MAXK: slots read
+// per chunk (top-k <= MAXK)
+template <bool SLOTS, int MAXCH, int MAXK>
 __global__ __launch_bounds__(kBndThreads) void boundary_kernel(
     const float* __restrict__ Y, int K, const int32_t* __restrict__ ids, int e_begin, int e_end,
     const void* __restrict__ y, int y_bf16, const uint16_t* h, const float* __restrict__ gp,
@@ -45,27 +49,38 @@ __global__ __launch_bounds__(kBndThreads) void boundary_kernel(
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const int nch = H / 4;
-  floatx4 u[kBndMaxChunks];
+  // slots of this token that contribute (all K, or those routed into [e_begin, e_end))
+  uint32_t slots = 0;
+  if constexpr (SLOTS) {
+    for (int k = 0; k < K; ++k) {
+      const bool in = !ids || (ids[t * K + k] >= e_begin && ids[t * K + k] < e_end);
+      slots |= (in ? 1u : 0u) << k;
+    }
+  }
+  floatx4 u[MAXCH];
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kBndMaxChunks; ++j) {
+  for (int j = 0; j < MAXCH; ++j) {
     const int ch = threadIdx.x + kBndThreads * j;
     u[j] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (ch >= nch) continue;
     const int c = 4 * ch;
     floatx4 v;
     if constexpr (SLOTS) {
+      // all of the chunk's slot reads issued together (read once: non-temporal), then summed in
+      // k order starting from the first contributing slot
       const float* yp = Y + t * K * H + c;
+      floatx4 yk[MAXK];
+#pragma unroll
+      for (int k = 0; k < MAXK; ++k)
+        if ((slots >> k) & 1u)
+          yk[k] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(yp + (int64_t)k * H));
       v = floatx4{0.f, 0.f, 0.f, 0.f};
       bool first = true;
-      for (int k = 0; k < K; ++k) {
-        if (ids) {
-          const int e = ids[t * K + k];
-          if (e < e_begin || e >= e_end) continue;
-        }
-        const floatx4 yk =   // read once: non-temporal
-            __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(yp + (int64_t)k * H));
-        v = first ? yk : v + yk;
+#pragma unroll
+      for (int k = 0; k < MAXK; ++k) {
+        if (!((slots >> k) & 1u)) continue;
+        v = first ? yk[k] : v + yk[k];
         first = false;
       }
     } else if (y_bf16) {
@@ -81,7 +96,7 @@ __global__ __launch_bounds__(kBndThreads) void boundary_kernel(
   const float r1 = 1.0f / sqrtf(block_sum(ss, red) / (float)H + eps);
   float ss2 = 0.f;
 #pragma unroll
-  for (int j = 0; j < kBndMaxChunks; ++j) {
+  for (int j = 0; j < MAXCH; ++j) {
     const int ch = threadIdx.x + kBndThreads * j;
     if (ch >= nch) continue;
     const int c = 4 * ch;
@@ -107,7 +122,7 @@ __global__ __launch_bounds__(kBndThreads) void boundary_kernel(
   }
   const float r2 = 1.0f / sqrtf(block_sum(ss2, red) / (float)H + eps);
 #pragma unroll
-  for (int j = 0; j < kBndMaxChunks; ++j) {
+  for (int j = 0; j < MAXCH; ++j) {
     const int ch = threadIdx.x + kBndThreads * j;
     if (ch >= nch) continue;
     const int c = 4 * ch;
@@ -127,14 +142,37 @@ hipError_t launch_boundary(const BoundaryArgs& b, const float* Y, int K, const i
                            int e_begin, int e_end, const void* y, bool y_bf16, int64_t T, int H,
                            hipStream_t st) {
   if (T == 0) return hipSuccess;
+  // registers sized to the hidden size: chunks per thread 4 / 8 / 16 (slot reads always sized for
+  // 16: an 8-slot instantiation lets the compiler hoist every chunk's reads at once, 250 registers
+  // and one wave per SIMD, measured 3.8x slower)
+  const int nch = ceil_div(H / 4, kBndThreads);
+  auto go = [&](auto slots_tag, auto ch_tag, auto k_tag) {
+    constexpr bool S = decltype(slots_tag)::value;
+    constexpr int CH = decltype(ch_tag)::value, MK = decltype(k_tag)::value;
+    if constexpr (S)
+      hipLaunchKernelGGL((boundary_kernel<true, CH, MK>), dim3((unsigned)T), dim3(kBndThreads), 0,
+                         st, Y, K, ids, e_begin, e_end, nullptr, 0, b.h, b.gamma_post,
+                         b.gamma_next, b.h_out, b.x_next, H, b.alpha, b.beta, b.eps);
+    else
+      hipLaunchKernelGGL((boundary_kernel<false, CH, MK>), dim3((unsigned)T), dim3(kBndThreads),
+                         0, st, nullptr, 0, nullptr, 0, 0, y, y_bf16 ? 1 : 0, b.h, b.gamma_post,
+                         b.gamma_next, b.h_out, b.x_next, H, b.alpha, b.beta, b.eps);
+  };
+  using T4 = std::integral_constant<int, 4>;
+  using T8 = std::integral_constant<int, 8>;
+  using T16 = std::integral_constant<int, 16>;
+  auto by_chunks = [&](auto slots_tag, auto k_tag) {
+    if (nch <= 4)
+      go(slots_tag, T4{}, k_tag);
+    else if (nch <= 8)
+      go(slots_tag, T8{}, k_tag);
+    else
+      go(slots_tag, T16{}, k_tag);
+  };
   if (Y)
-    hipLaunchKernelGGL(boundary_kernel<true>, dim3((unsigned)T), dim3(kBndThreads), 0, st, Y, K,
-                       ids, e_begin, e_end, nullptr, 0, b.h, b.gamma_post, b.gamma_next, b.h_out,
-                       b.x_next, H, b.alpha, b.beta, b.eps);
+    by_chunks(std::true_type{}, T16{});
   else
-    hipLaunchKernelGGL(boundary_kernel<false>, dim3((unsigned)T), dim3(kBndThreads), 0, st,
-                       nullptr, 0, nullptr, 0, 0, y, y_bf16 ? 1 : 0, b.h, b.gamma_post,
-                       b.gamma_next, b.h_out, b.x_next, H, b.alpha, b.beta, b.eps);
+    by_chunks(std::false_type{}, T16{});
   return hipGetLastError();
 }
 
