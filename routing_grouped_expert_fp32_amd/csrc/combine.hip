@@ -14,6 +14,8 @@ namespace beam {
 // Y is read once: non-temporal loads (measured 17% faster than cached ones at T=8192).
 // FILTER: only slots whose id lies in [e_begin, e_end) contribute (a routed call over a range of
 // experts; the other slots' Y rows were never written); the sum then starts from +0.
+constexpr int kCombineMaxSlots = 16;   // top-k <= 16
+
 template <bool FILTER>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       void* __restrict__ out, int out_bf16,
@@ -24,18 +26,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= H) return;
   const float* y = Y + t * K * H + c;
+  // contributing slots (all K, or those routed into [e_begin, e_end)); their reads are issued
+  // together, then summed in k order
+  uint32_t slots = K >= 32 ? ~0u : (1u << K) - 1u;
+  if constexpr (FILTER) {
+    slots = 0;
+    for (int k = 0; k < K; ++k)
+      slots |= (ids[t * K + k] >= e_begin && ids[t * K + k] < e_end ? 1u : 0u) << k;
+  }
+  floatx4 yk[kCombineMaxSlots];
+#pragma unroll
+  for (int k = 0; k < kCombineMaxSlots; ++k)
+    if ((slots >> k) & 1u)
+      yk[k] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(y + (int64_t)k * H));
   floatx4 acc;
   if constexpr (FILTER) {
     acc = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[t * K + k];
-      if (e >= e_begin && e < e_end)
-        acc += __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(y + (int64_t)k * H));
-    }
+#pragma unroll
+    for (int k = 0; k < kCombineMaxSlots; ++k)
+      if ((slots >> k) & 1u) acc += yk[k];
   } else {
-    acc = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(y));
-    for (int k = 1; k < K; ++k)
-      acc += __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(y + (int64_t)k * H));
+    acc = yk[0];
+#pragma unroll
+    for (int k = 1; k < kCombineMaxSlots; ++k)
+      if ((slots >> k) & 1u) acc += yk[k];
   }
   if (out_bf16) {
     u32x2 p;
