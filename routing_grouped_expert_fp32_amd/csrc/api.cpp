@@ -331,6 +331,33 @@ bool boundary_alias(const std::vector<Range>& ins_except_h, const Range& h, cons
   return any_alias(ins, outs);
 }
 
+// A dense SwiGLU layer as a one-expert block: E = G = Gk = K = 1, weight 1.
+beam_moe_cfg dense_cfg(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t out_dtype) {
+  return beam_moe_cfg{hidden, 1, 1, 1, 1, d_ff, 1.0f, BEAM_BF16, w_dtype, out_dtype};
+}
+
+beam_status_t check_dense(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t out_dtype,
+                          int64_t T) {
+  if (hidden <= 0 || d_ff <= 0 || T < 0) return BEAM_ERR_SHAPE;
+  if (w_dtype != BEAM_BF16 && w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
+  if (out_dtype != BEAM_F32 && out_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
+  if (hidden % 256 != 0 || d_ff % 256 != 0 || (int64_t)hidden * d_ff >= (int64_t(1) << 31) ||
+      T >= (int64_t(1) << 31))
+    return BEAM_ERR_UNSUPPORTED;
+  return BEAM_OK;
+}
+
+// Largest K split the dense down GEMM may take (tiled blocks; parts of at least 16 stages). The
+// workspace holds that many partial rows per token, so its size does not depend on the device.
+int dense_ksplit_max(const beam_moe_cfg& c, int64_t T) {
+  if (use_small_blocks(c, T)) return 1;
+  const int64_t k_stages = (int64_t)c.d_ff * dtype_bytes(c.w_dtype) / 128;
+  int m = 1;
+  for (int ks = 2; ks <= 4; ks *= 2)
+    if (k_stages % ks == 0 && k_stages / ks >= 16) m = ks;
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
@@ -603,33 +630,6 @@ beam_status_t beam_moe_forward_routed(const void* x, const int32_t* topk_ids, co
   return run_experts(c, T, L, reinterpret_cast<char*>(workspace), topk_ids, topk_w, x, w_gate_up,
                      w_down, w_gate_up_scale, w_down_scale, out, expert_begin,
                      expert_end - expert_begin, true, st);
-}
-
-// A dense SwiGLU layer as a one-expert block: E = G = Gk = K = 1, weight 1.
-beam_moe_cfg dense_cfg(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t out_dtype) {
-  return beam_moe_cfg{hidden, 1, 1, 1, 1, d_ff, 1.0f, BEAM_BF16, w_dtype, out_dtype};
-}
-
-beam_status_t check_dense(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t out_dtype,
-                          int64_t T) {
-  if (hidden <= 0 || d_ff <= 0 || T < 0) return BEAM_ERR_SHAPE;
-  if (w_dtype != BEAM_BF16 && w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
-  if (out_dtype != BEAM_F32 && out_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
-  if (hidden % 256 != 0 || d_ff % 256 != 0 || (int64_t)hidden * d_ff >= (int64_t(1) << 31) ||
-      T >= (int64_t(1) << 31))
-    return BEAM_ERR_UNSUPPORTED;
-  return BEAM_OK;
-}
-
-// Largest K split the dense down GEMM may take (tiled blocks; parts of at least 16 stages). The
-// workspace holds that many partial rows per token, so its size does not depend on the device.
-int dense_ksplit_max(const beam_moe_cfg& c, int64_t T) {
-  if (use_small_blocks(c, T)) return 1;
-  const int64_t k_stages = (int64_t)c.d_ff * dtype_bytes(c.w_dtype) / 128;
-  int m = 1;
-  for (int ks = 2; ks <= 4; ks *= 2)
-    if (k_stages % ks == 0 && k_stages / ks >= 16) m = ks;
-  return m;
 }
 
 size_t beam_dense_mlp_workspace_bytes(int32_t hidden, int32_t d_ff, int32_t w_dtype, int64_t T) {
