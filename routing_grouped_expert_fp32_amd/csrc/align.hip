@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
                                                             const uint64_t* __restrict__ chunk_mask,
                                                             const int32_t* __restrict__ chunk_base,
                                                             const int32_t* __restrict__ expert_off,
+                                                            const float* __restrict__ topk_w,
                                                             int32_t* __restrict__ sorted_slot,
+                                                            float* __restrict__ sorted_w,
                                                             int64_t T, int E, int K, int e_begin) {
   __shared__ unsigned long long mask[256 * kWords];
   __shared__ int base[256];
@@ -174,6 +176,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
     const uint64_t below = (tl & 63) ? (mask[e * kWords + w] & ((1ull << (tl & 63)) - 1ull)) : 0ull;
     rank += __popcll(below);
     sorted_slot[base[e] + rank] = (int32_t)(tbeg * K + i);
+    sorted_w[base[e] + rank] = topk_w[tbeg * K + i];
   }
 }
 
@@ -183,8 +186,8 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
 // experts in LDS, the same block table and the same stable token order as the three-kernel path.
 static_assert(kSmallRouteT <= 64, "one mask word per expert");
 
-__device__ void align_small_body(const int32_t* sid, int64_t T, int E, int K, int e_begin, int BM,
-                                 const AlignTables& at) {
+__device__ void align_small_body(const int32_t* sid, const float* tw, int64_t T, int E, int K,
+                                 int e_begin, int BM, const AlignTables& at) {
   __shared__ unsigned long long mask[256];
   __shared__ int rows_scan[256];
   __shared__ int blks_scan[256];
@@ -239,13 +242,15 @@ __device__ void align_small_body(const int32_t* sid, int64_t T, int E, int K, in
     const int t = i / K;
     const int rank = __popcll(mask[e] & ((1ull << t) - 1ull));
     at.sorted_slot[rows_scan[e] - __popcll(mask[e]) + rank] = i;
+    at.sorted_w[rows_scan[e] - __popcll(mask[e]) + rank] = tw[i];
   }
 }
 
 __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __restrict__ ids,
+                                                           const float* __restrict__ tw,
                                                            AlignTables at, int64_t T, int E, int K,
                                                            int e_begin, int BM) {
-  align_small_body(ids, T, E, K, e_begin, BM, at);
+  align_small_body(ids, tw, T, E, K, e_begin, BM, at);
 }
 
 // Routes of a dense layer run as one expert: every token's single slot goes to expert 0 with
@@ -266,12 +271,12 @@ hipError_t launch_fill_dense_routes(int32_t* ids, float* w, int64_t n, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
-                        int e_begin, int e_count, hipStream_t st) {
+hipError_t launch_align(const int32_t* ids, const float* topk_w, const AlignTables& at,
+                        const Shape& s, int BM, int e_begin, int e_count, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   if (s.T <= kSmallRouteT) {
-    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, st, ids, at, s.T, e_count, s.K,
-                       e_begin, BM);
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, st, ids, topk_w, at, s.T,
+                       e_count, s.K, e_begin, BM);
     return hipGetLastError();
   }
   const int n_chunks = (int)ceil_div(s.T, kChunk);
@@ -285,7 +290,8 @@ hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& 
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(align_scatter_kernel, dim3(n_chunks), dim3(256), 0, st, ids, at.chunk_mask,
-                     at.chunk_base, at.expert_off, at.sorted_slot, s.T, e_count, s.K, e_begin);
+                     at.chunk_base, at.expert_off, topk_w, at.sorted_slot, at.sorted_w, s.T,
+                     e_count, s.K, e_begin);
   return hipGetLastError();
 }
 

@@ -47,8 +47,8 @@ int block_rows(const beam_moe_cfg& c, int64_t T) {
 
 struct Layout {
   size_t sb = 0, ids = 0, w = 0, chunk_mask = 0, chunk_base = 0, expert_count = 0, expert_off = 0,
-         n_blocks = 0, blk_expert = 0, blk_row0 = 0, blk_rows = 0, sorted = 0, hbuf = 0, ybuf = 0,
-         xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
+         n_blocks = 0, blk_expert = 0, blk_row0 = 0, blk_rows = 0, sorted = 0, sorted_w = 0, hbuf = 0,
+         ybuf = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
   int64_t max_blocks = 0;
   int bm = 0;
 };
@@ -83,6 +83,7 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full, int ybuf_parts =
     L.blk_row0 = take(sizeof(int32_t) * (size_t)L.max_blocks);
     L.blk_rows = take(sizeof(int32_t) * (size_t)L.max_blocks);
     L.sorted = take(sizeof(int32_t) * (size_t)TK);
+    L.sorted_w = take(sizeof(float) * (size_t)TK);
     const size_t hel = c.w_dtype == BEAM_F32 ? 4 : 2;
     L.hbuf = take(hel * (size_t)TK * (size_t)c.d_ff);
     L.ybuf = take(sizeof(float) * (size_t)TK * (size_t)ybuf_parts * (size_t)c.hidden);
@@ -231,6 +232,7 @@ beam::AlignTables align_tables(const Layout& L, char* ws) {
   at.blk_row0 = reinterpret_cast<int32_t*>(ws + L.blk_row0);
   at.blk_rows = reinterpret_cast<int32_t*>(ws + L.blk_rows);
   at.sorted_slot = reinterpret_cast<int32_t*>(ws + L.sorted);
+  at.sorted_w = reinterpret_cast<float*>(ws + L.sorted_w);
   return at;
 }
 
@@ -250,7 +252,7 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
   const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
 
   if (e_count > 0) {
-    LAUNCH(2, beam::launch_align(ids, at, s, L.bm, e_begin, e_count, st));
+    LAUNCH(2, beam::launch_align(ids, tw, at, s, L.bm, e_begin, e_count, st));
     if (c.w_dtype == BEAM_F32) {
       float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
       LAUNCH(4, beam::launch_gate_up_f32(reinterpret_cast<const float*>(x),

@@ -47,6 +47,7 @@ struct AlignTables {
   int32_t* blk_row0;      // [max_blocks] first sorted row of the block
   int32_t* blk_rows;      // [max_blocks] rows in the block (1..BM)
   int32_t* sorted_slot;   // [T*K] slot id (t*K+k) of each sorted row
+  float* sorted_w;        // [T*K] routing weight of each sorted row (topk_w[sorted_slot[i]])
 };
 
 
@@ -83,8 +84,8 @@ hipError_t launch_router_select_partials(const float* part, const float* bias, i
 hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const Shape& s,
                                 hipStream_t st);
 hipError_t launch_fill_dense_routes(int32_t* ids, float* w, int64_t n, hipStream_t st);
-hipError_t launch_align(const int32_t* ids, const AlignTables& at, const Shape& s, int BM,
-                        int e_begin, int e_count, hipStream_t st);
+hipError_t launch_align(const int32_t* ids, const float* topk_w, const AlignTables& at,
+                        const Shape& s, int BM, int e_begin, int e_count, hipStream_t st);
 // bf16 or FP8 experts; FP8 needs the activation scales (per token for x, per sorted row for h)
 // and the per-output-channel weight scales.
 hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const float* x_scale,

@@ -24,7 +24,10 @@
 //     on the same XCD).
 // Epilogues: gate/up  h = bf16( silu(bf16(g)) * bf16(u) ), g/u dequantised first for FP8
 //            (acc * token scale * output-channel scale); down  Y[slot] = topk_w[slot] * y (FP32),
-//            y = acc (* row scale * output-channel scale for FP8).
+//            y = acc (* row scale * output-channel scale for FP8). The down step's per-row slot
+//            ids and weights (and FP8 scales) are loaded into LDS at the start, ahead of the first
+//            stage, so its epilogue issues stores only (12-16% of the down GEMM's time went to
+//            the epilogue's dependent loads and stores).
 #pragma once
 #include <type_traits>
 
@@ -119,7 +122,11 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   using M = PipeMath<FP8>;
   using C = PipeCfg<FP8>;
   constexpr int WAVES = C::WAVES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLdsBytes];
+  // one LDS array (a second __shared__ object makes the compiler wait for every direct load
+  // right after issuing it): rings, then the down epilogue's operands
+  constexpr int kEpiBytes = GATE_UP ? 0 : (FP8 ? 12 * C::BM + 4 * kPBN : 8 * C::BM);
+  static_assert(C::kLdsBytes + kEpiBytes <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLdsBytes + kEpiBytes];
   unsigned char* const aring = smem;
   unsigned char* const bring = smem + C::AST * C::kAStageBytes;
   // ---- tile assignment (XCD-aware) ----
@@ -201,8 +208,35 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // Issue order: prologue A(0), B(0); iteration kt waits for everything it issued, passes the
   // barrier (every wave's loads of stage kt have landed and every wave is done reading stage
   // kt - 1, whose slots are reused), then issues A(kt+1), B(kt+1) and computes stage kt.
+  // down: epilogue operands of this tile (independent loads, issued before the first stage's, and
+  // stored to LDS behind them; the loop's first wait covers both)
+  int* const e_slot = reinterpret_cast<int*>(smem + C::kLdsBytes);
+  float* const e_w = reinterpret_cast<float*>(smem + C::kLdsBytes + 4 * C::BM);
+  float* const e_as = reinterpret_cast<float*>(smem + C::kLdsBytes + 8 * C::BM);
+  float* const e_ws = reinterpret_cast<float*>(smem + C::kLdsBytes + 12 * C::BM);
+  int v_slot = 0;
+  float v_w = 0.f, v_as = 0.f, v_ws = 0.f;
+  if constexpr (!GATE_UP) {
+    static_assert(C::BM <= 64 * WAVES && kPBN <= 64 * WAVES, "one row / column per thread");
+    if (tid < rows) {
+      v_slot = at.sorted_slot[row0 + tid];
+      v_w = at.sorted_w[row0 + tid];
+      if constexpr (FP8) v_as = a_scale[row0 + tid];
+    }
+    if constexpr (FP8)
+      if (tid < kPBN) v_ws = w_scale[(int64_t)e * Nout + 256 * j + tid];
+  }
   issue_a(0);
   issue_b(0);
+  if constexpr (!GATE_UP) {
+    if (tid < C::BM) {
+      e_slot[tid] = v_slot;
+      e_w[tid] = v_w;
+      if constexpr (FP8) e_as[tid] = v_as;
+    }
+    if constexpr (FP8)
+      if (tid < kPBN) e_ws[tid] = v_ws;
+  }
 
   // fragment byte offsets of this lane inside a 16-row group, per MFMA step of a stage:
   // row r = lane % 16, chunk M::chunk(step, lane / 16, half) (swizzled)
@@ -287,6 +321,7 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
     kloop(std::integral_constant<int, 2>{});
 
   // ---- epilogue ----
+  if constexpr (!GATE_UP) __syncthreads();   // the staged operands are visible
 #pragma unroll
   for (int i = 0; i < NVMAX; ++i) {
     const int mt = wm + WMW * i;
@@ -310,13 +345,13 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
               (uint16_t)f32_to_bf16_bits(h);
         }
       } else {
-        const int slot = at.sorted_slot[row0 + row];
-        const float wgt = topk_w[slot];
+        const int slot = e_slot[row];
+        const float wgt = e_w[row];
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const int col = 256 * j + 128 * wn + 16 * n + r;
+          const int tc = 128 * wn + 16 * n + r, col = 256 * j + tc;
           float y = acc[i][n][q];
-          if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
+          if constexpr (FP8) y = y * e_as[row] * e_ws[tc];
           reinterpret_cast<float*>(out)[((int64_t)slot * ksplit + ksp) * Nout + col] = wgt * y;
         }
       }
