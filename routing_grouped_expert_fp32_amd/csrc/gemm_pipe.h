@@ -24,10 +24,11 @@
 //     on the same XCD).
 // Epilogues: gate/up  h = bf16( silu(bf16(g)) * bf16(u) ), g/u dequantised first for FP8
 //            (acc * token scale * output-channel scale); down  Y[slot] = topk_w[slot] * y (FP32),
-//            y = acc (* row scale * output-channel scale for FP8). The down step's per-row slot
-//            ids and weights (and FP8 scales) are loaded into LDS at the start, ahead of the first
-//            stage, so its epilogue issues stores only (12-16% of the down GEMM's time went to
-//            the epilogue's dependent loads and stores).
+//            y = acc (* row scale * output-channel scale for FP8). The epilogue operands (down: each
+//            row's slot id and routing weight; FP8: the row or token scales and the tile's output-
+//            channel scales) are loaded into LDS at the start, behind the first stage's loads, so
+//            the epilogue issues stores only (12-16% of the down GEMM's time went to the
+//            epilogue's dependent loads and stores).
 #pragma once
 #include <type_traits>
 
@@ -123,8 +124,9 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   using C = PipeCfg<FP8>;
   constexpr int WAVES = C::WAVES;
   // one LDS array (a second __shared__ object makes the compiler wait for every direct load
-  // right after issuing it): rings, then the down epilogue's operands
-  constexpr int kEpiBytes = GATE_UP ? 0 : (FP8 ? 12 * C::BM + 4 * kPBN : 8 * C::BM);
+  // right after issuing it): rings, then the epilogue's operands
+  constexpr int kEpiBytes = GATE_UP ? (FP8 ? 12 * C::BM + 4 * kPBN : 0)
+                                    : (FP8 ? 12 * C::BM + 4 * kPBN : 8 * C::BM);
   static_assert(C::kLdsBytes + kEpiBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLdsBytes + kEpiBytes];
   unsigned char* const aring = smem;
@@ -208,8 +210,8 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // Issue order: prologue A(0), B(0); iteration kt waits for everything it issued, passes the
   // barrier (every wave's loads of stage kt have landed and every wave is done reading stage
   // kt - 1, whose slots are reused), then issues A(kt+1), B(kt+1) and computes stage kt.
-  // down: epilogue operands of this tile (independent loads, issued before the first stage's, and
-  // stored to LDS behind them; the loop's first wait covers both)
+  // epilogue operands of this tile: loads issued before the first stage's (FP8 gate/up: the token
+  // scale, which needs the slot id, behind them) and stored to LDS once they have landed
   int* const e_slot = reinterpret_cast<int*>(smem + C::kLdsBytes);
   float* const e_w = reinterpret_cast<float*>(smem + C::kLdsBytes + 4 * C::BM);
   float* const e_as = reinterpret_cast<float*>(smem + C::kLdsBytes + 8 * C::BM);
@@ -225,10 +227,16 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
     }
     if constexpr (FP8)
       if (tid < kPBN) v_ws = w_scale[(int64_t)e * Nout + 256 * j + tid];
+  } else if constexpr (FP8) {   // tile columns: 128 gate channels, then the matching up channels
+    if (tid < rows) v_slot = at.sorted_slot[row0 + tid];
+    if (tid < kPBN)
+      v_ws = w_scale[(int64_t)e * 2 * Nout + (tid < 128 ? 128 * j + tid : Nout + 128 * j + tid - 128)];
   }
   issue_a(0);
   issue_b(0);
-  if constexpr (!GATE_UP) {
+  if constexpr (GATE_UP && FP8)
+    if (tid < rows) v_as = a_scale[v_slot / topk];
+  if constexpr (!GATE_UP || FP8) {
     if (tid < C::BM) {
       e_slot[tid] = v_slot;
       e_w[tid] = v_w;
@@ -321,7 +329,7 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
     kloop(std::integral_constant<int, 2>{});
 
   // ---- epilogue ----
-  if constexpr (!GATE_UP) __syncthreads();   // the staged operands are visible
+  if constexpr (!GATE_UP || FP8) __syncthreads();   // the staged operands are visible
 #pragma unroll
   for (int i = 0; i < NVMAX; ++i) {
     const int mt = wm + WMW * i;
@@ -331,14 +339,14 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
       if (row >= rows) continue;
       if constexpr (GATE_UP) {
         float sx = 1.f;
-        if constexpr (FP8) sx = a_scale[at.sorted_slot[row0 + row] / topk];
+        if constexpr (FP8) sx = e_as[row];
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const int hcol = 128 * j + 64 * wn + 16 * n + r;
+          const int tc = 64 * wn + 16 * n + r, hcol = 128 * j + tc;
           float gv = acc[i][n][q], uv = acc[i][n + 4][q];
           if constexpr (FP8) {
-            gv = gv * sx * w_scale[(int64_t)e * 2 * Nout + hcol];
-            uv = uv * sx * w_scale[(int64_t)e * 2 * Nout + Nout + hcol];
+            gv = gv * sx * e_ws[tc];
+            uv = uv * sx * e_ws[128 + tc];
           }
           const float h = silu_f32(bf16_round(gv)) * bf16_round(uv);
           reinterpret_cast<uint16_t*>(out)[(int64_t)(row0 + row) * Nout + hcol] =
