@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void grouped_small_kernel(
       const int slot = at.sorted_slot[row0 + row];
       float y = acc0[i];
       if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
-      reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = topk_w[slot] * y;
+      reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = at.sorted_w[row0 + row] * y;
     }
   }
 }
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void grouped_small_ks_kernel(
       const int slot = at.sorted_slot[row0 + row];
       float y = s0[q];
       if constexpr (FP8) y = y * a_scale[row0 + row] * w_scale[(int64_t)e * Nout + col];
-      reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = topk_w[slot] * y;
+      reinterpret_cast<float*>(out)[(int64_t)slot * Nout + col] = at.sorted_w[row0 + row] * y;
     }
   }
 }
