@@ -362,8 +362,11 @@ def roofline(r, workload):
         pk = PEAK_TFLOPS[r["dtype"]]
         roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": pk, "unit": "TFLOP/s",
                 "frac": g["TFLOPs"] / pk}
-    kind = "small_ks" if r["small_blocks"] else "pipe"
-    roof["kernel"] = f"gate_up: grouped_{kind}_kernel<true, {str(r['dtype'] == 'fp8').lower()}>"
+    fp8 = str(r["dtype"] == "fp8").lower()
+    if r["small_blocks"]:   # K split over 8 waves (bf16) or 4 (FP8) at the Beam shape
+        roof["kernel"] = f"gate_up: grouped_small_ks_kernel<true, {fp8}, {4 if fp8 == 'true' else 8}>"
+    else:
+        roof["kernel"] = f"gate_up: grouped_pipe_kernel<true, {fp8}>"
     roof["algorithmic_bytes_per_launch"] = g["bytes"]
     roof["traffic"] = None
     cpath = os.path.join(ROOT, "profiles", f"counters_{workload}.json")

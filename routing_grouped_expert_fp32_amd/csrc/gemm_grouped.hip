@@ -33,19 +33,26 @@ static void launch_one(const void* a, const void* w, const float* topk_w, void* 
   const auto* A = reinterpret_cast<const unsigned char*>(a);
   const auto* W = reinterpret_cast<const unsigned char*>(w);
   if (small) {
-    // K split across the waves of 16-column (down: 32-column) workgroups: 4x the workgroups of the
-    // column-tiled grid (which leaves most CUs idle at a handful of tokens) and two batches in
-    // flight per wave; faster at every decode size measured (T = 1 .. 64). The column-tiled kernel
-    // covers the shapes whose quarter rows are not whole batches.
+    // K split across the waves of 16-column (down: 32-column) workgroups: 4x or 8x the workgroups
+    // of the column-tiled grid (which leaves most CUs idle at a handful of tokens) and two batches
+    // in flight per wave; faster at every decode size measured (T = 1 .. 64). The column-tiled
+    // kernel covers the shapes whose rows do not split into whole batches.
     const int64_t row_bytes = (int64_t)Kd * (FP8 ? 1 : 2);
-    const bool ks = (row_bytes / 4) % KsBatch<FP8>::kBytes == 0;
-    if (ks) {
-      dim3 grid(Nout / (GATE_UP ? 16 : 32), (unsigned)max_blocks);
-      hipLaunchKernelGGL((grouped_small_ks_kernel<GATE_UP, FP8>), grid, dim3(256), 0, st, A, W,
+    constexpr int64_t BB = KsBatch<FP8>::kBytes;
+    const dim3 grid(Nout / (GATE_UP ? 16 : 32), (unsigned)max_blocks);
+    if constexpr (GATE_UP && !FP8) {
+      if ((row_bytes / 8) % BB == 0) {
+        hipLaunchKernelGGL((grouped_small_ks_kernel<GATE_UP, FP8, 8>), grid, dim3(512), 0, st, A,
+                           W, topk_w, out, at, Kd, Nout, topk, a_scale, w_scale);
+        return;
+      }
+    }
+    if ((row_bytes / 4) % BB == 0) {
+      hipLaunchKernelGGL((grouped_small_ks_kernel<GATE_UP, FP8, 4>), grid, dim3(256), 0, st, A, W,
                          topk_w, out, at, Kd, Nout, topk, a_scale, w_scale);
     } else {
-      dim3 grid(Nout / kSmallCols, (unsigned)max_blocks);
-      hipLaunchKernelGGL((grouped_small_kernel<GATE_UP, FP8>), grid, dim3(256), 0, st, A, W,
+      hipLaunchKernelGGL((grouped_small_kernel<GATE_UP, FP8>),
+                         dim3(Nout / kSmallCols, (unsigned)max_blocks), dim3(256), 0, st, A, W,
                          topk_w, out, at, Kd, Nout, topk, a_scale, w_scale);
     }
   } else {

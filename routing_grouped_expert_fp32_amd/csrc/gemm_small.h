@@ -132,11 +132,12 @@ __global__ __launch_bounds__(256) void grouped_small_kernel(
 
 // K-split variant: a WG covers 16 h columns (gate/up: each lane streams a gate row and the
 // matching up row) or 32 output columns (down: two 16-column groups, so a down workgroup streams as
-// many weight bytes as a gate/up one; measured 0.516 -> 0.503 ms at T=32), and its 4 waves split K
-// into quarters (4x the workgroups of the column-tiled kernel, which matters when a handful of
-// tokens touch few experts). Each wave keeps two batches of loads in flight (the next batch is
-// issued before the current one's MFMAs); the four partial tiles are summed in LDS in wave order
-// (deterministic) and wave 0 runs the epilogue. Requires (row bytes / 4) % kKsBatchBytes == 0.
+// many weight bytes as a gate/up one; measured 0.516 -> 0.503 ms at T=32), and its waves (4 or 8,
+// KSW) split K into equal parts (many more workgroups than the column-tiled kernel, which
+// matters when a handful of tokens touch few experts). Each wave keeps two batches of loads in
+// flight (the next batch is issued before the current one's MFMAs); the partial tiles are summed
+// in LDS in wave order (deterministic) and wave 0 runs the epilogue. Requires the rows' parts to
+// be whole batches.
 template <bool FP8>
 struct KsBatch {
   static constexpr int kBytes = 256;   // bf16: 4 steps of 64 B; FP8: 2 steps of 128 B
@@ -146,15 +147,20 @@ struct KsBatch<true> {
   static constexpr int kBytes = 128;   // one 128-deep FP8 step (the quarter of 2560 is 640 B)
 };
 
-template <bool GATE_UP, bool FP8>
-__global__ __launch_bounds__(256) void grouped_small_ks_kernel(
+// KSW = waves splitting K: 8 for bf16 gate/up where its rows split into whole batches
+// (shorter-lived workgroups, so less of the grid's tail runs part-empty: 0.996 -> 0.986 ms at
+// T=32), else 4 (FP8 gate/up measured 6% slower with 8: its eighths of a row are 5 one-step
+// batches).
+template <bool GATE_UP, bool FP8, int KSW>
+__global__ __launch_bounds__(64 * KSW) void grouped_small_ks_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
     const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
   using M = SmallMath<FP8>;
   constexpr int U = KsBatch<FP8>::kBytes / M::kStepBytes;   // MFMA steps per batch
   constexpr int NACC = 2;   // gate/up: a gate and an up row per lane; down: two 16-column groups
-  __shared__ floatx4 red[4][NACC][64];
+  constexpr int kKsWaves = KSW;
+  __shared__ floatx4 red[kKsWaves][NACC][64];
   const int b = blockIdx.y;
   if (b >= at.n_blocks[0]) return;
   const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(256) void grouped_small_ks_kernel(
   const int r = lane & 15, g = lane >> 4;
   const int c0 = blockIdx.x * (GATE_UP ? 16 : 32);
   const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
-  const int64_t kq = row_bytes / 4, kbeg = wave * kq;
+  const int64_t kq = row_bytes / kKsWaves, kbeg = wave * kq;
 
   const unsigned char* ap = nullptr;
   if (r < rows) {
@@ -216,8 +222,12 @@ __global__ __launch_bounds__(256) void grouped_small_ks_kernel(
   red[wave][1][lane] = acc1;
   __syncthreads();
   if (wave != 0) return;
-  floatx4 s0 = ((red[0][0][lane] + red[1][0][lane]) + red[2][0][lane]) + red[3][0][lane];
-  const floatx4 s1 = ((red[0][1][lane] + red[1][1][lane]) + red[2][1][lane]) + red[3][1][lane];
+  floatx4 s0 = red[0][0][lane], s1 = red[0][1][lane];
+#pragma unroll
+  for (int w = 1; w < kKsWaves; ++w) {
+    s0 += red[w][0][lane];
+    s1 += red[w][1][lane];
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = 4 * g + q;
