@@ -264,7 +264,7 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
       uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
       LAUNCH(4, beam::launch_gate_up(x, w_gate_up, hbuf, nullptr, nullptr, false, at, s,
                                      L.max_blocks, small, st));
-      LAUNCH(6, beam::launch_down(hbuf, w_down, nullptr, nullptr, false, tw, ybuf, at, s,
+      LAUNCH(6, beam::launch_down(hbuf, w_down, nullptr, nullptr, false, ybuf, at, s,
                                   L.max_blocks, small, st, ksplit));
     } else {
       uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.hbuf);
@@ -277,7 +277,7 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
       LAUNCH(4, beam::launch_gate_up(xq, w_gate_up, hbuf, xs, w_gate_up_scale, true, at, s,
                                      L.max_blocks, small, st));
       LAUNCH(5, beam::launch_quant_rows_fp8(hbuf, T * c.topk, c.d_ff, hq, hs, st));
-      LAUNCH(6, beam::launch_down(hq, w_down, hs, w_down_scale, true, tw, ybuf, at, s,
+      LAUNCH(6, beam::launch_down(hq, w_down, hs, w_down_scale, true, ybuf, at, s,
                                   L.max_blocks, small, st, ksplit));
     }
   }

@@ -91,12 +91,12 @@ hipError_t launch_align(const int32_t* ids, const float* topk_w, const AlignTabl
 hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const float* x_scale,
                           const float* w_scale, bool fp8, const AlignTables& at, const Shape& s,
                           int64_t max_blocks, bool small, hipStream_t st);
-// ksplit > 1 (tiled blocks only, stages of a row divisible by it): the down GEMM's K range is cut
-// into ksplit parts whose partial sums go to rows slot * ksplit + part of ybuf.
+// Each row's routing weight comes from the align tables (sorted_w). ksplit > 1 (tiled blocks only,
+// stages of a row divisible by it): the down GEMM's K range is cut into ksplit parts whose partial
+// sums go to rows slot * ksplit + part of ybuf.
 hipError_t launch_down(const void* h, const void* w_dn, const float* h_scale, const float* w_scale,
-                       bool fp8, const float* topk_w, float* ybuf, const AlignTables& at,
-                       const Shape& s, int64_t max_blocks, bool small, hipStream_t st,
-                       int ksplit = 1);
+                       bool fp8, float* ybuf, const AlignTables& at, const Shape& s,
+                       int64_t max_blocks, bool small, hipStream_t st, int ksplit = 1);
 // K split (1, 2 or 4) for a tiled down GEMM of `tiles` (block, column tile) workgroups over
 // `k_stages` 128-byte stages on a GPU of n_cu compute units.
 int down_ksplit(int64_t tiles, int64_t k_stages, int n_cu);

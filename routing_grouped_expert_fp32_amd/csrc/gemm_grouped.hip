@@ -26,7 +26,7 @@ int small_block_rows() { return kSmallBM; }
 int tiled_block_rows(bool fp8) { return fp8 ? PipeCfg<true>::BM : PipeCfg<false>::BM; }
 
 template <bool GATE_UP, bool FP8>
-static void launch_one(const void* a, const void* w, const float* topk_w, void* out,
+static void launch_one(const void* a, const void* w, void* out,
                        const float* a_scale, const float* w_scale, const AlignTables& at,
                        int Kd, int Nout, int topk, int64_t max_blocks, bool small,
                        hipStream_t st, int ksplit = 1) {
@@ -43,23 +43,23 @@ static void launch_one(const void* a, const void* w, const float* topk_w, void* 
     if constexpr (GATE_UP && !FP8) {
       if ((row_bytes / 8) % BB == 0) {
         hipLaunchKernelGGL((grouped_small_ks_kernel<GATE_UP, FP8, 8>), grid, dim3(512), 0, st, A,
-                           W, topk_w, out, at, Kd, Nout, topk, a_scale, w_scale);
+                           W, out, at, Kd, Nout, topk, a_scale, w_scale);
         return;
       }
     }
     if ((row_bytes / 4) % BB == 0) {
       hipLaunchKernelGGL((grouped_small_ks_kernel<GATE_UP, FP8, 4>), grid, dim3(256), 0, st, A, W,
-                         topk_w, out, at, Kd, Nout, topk, a_scale, w_scale);
+                         out, at, Kd, Nout, topk, a_scale, w_scale);
     } else {
       hipLaunchKernelGGL((grouped_small_kernel<GATE_UP, FP8>),
                          dim3(Nout / kSmallCols, (unsigned)max_blocks), dim3(256), 0, st, A, W,
-                         topk_w, out, at, Kd, Nout, topk, a_scale, w_scale);
+                         out, at, Kd, Nout, topk, a_scale, w_scale);
     }
   } else {
     const int n_ctiles = GATE_UP ? Nout / 128 : Nout / 256;
     const int64_t wgs = 8 * ceil_div(max_blocks * n_ctiles * ksplit, 8);
     hipLaunchKernelGGL((grouped_pipe_kernel<GATE_UP, FP8>), dim3((unsigned)wgs),
-                       dim3(64 * PipeCfg<FP8>::WAVES), 0, st, A, W, topk_w, out, at, Kd, Nout, topk,
+                       dim3(64 * PipeCfg<FP8>::WAVES), 0, st, A, W, out, at, Kd, Nout, topk,
                        n_ctiles, a_scale, w_scale, ksplit);
   }
 }
@@ -69,26 +69,25 @@ hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const
                           int64_t max_blocks, bool small, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   if (fp8)
-    launch_one<true, true>(x, w_gu, nullptr, hbuf, x_scale, w_scale, at, s.H, s.F, s.K,
+    launch_one<true, true>(x, w_gu, hbuf, x_scale, w_scale, at, s.H, s.F, s.K,
                            max_blocks, small, st);
   else
-    launch_one<true, false>(x, w_gu, nullptr, hbuf, nullptr, nullptr, at, s.H, s.F, s.K,
+    launch_one<true, false>(x, w_gu, hbuf, nullptr, nullptr, at, s.H, s.F, s.K,
                             max_blocks, small, st);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const void* h, const void* w_dn, const float* h_scale, const float* w_scale,
-                       bool fp8, const float* topk_w, float* ybuf, const AlignTables& at,
-                       const Shape& s, int64_t max_blocks, bool small, hipStream_t st,
-                       int ksplit) {
+                       bool fp8, float* ybuf, const AlignTables& at, const Shape& s,
+                       int64_t max_blocks, bool small, hipStream_t st, int ksplit) {
   if (s.T == 0) return hipSuccess;
   if (ksplit != 1 && (small || (s.F * (fp8 ? 1 : 2) / kPRowBytes) % ksplit != 0))
     return hipErrorInvalidValue;
   if (fp8)
-    launch_one<false, true>(h, w_dn, topk_w, ybuf, h_scale, w_scale, at, s.F, s.H, s.K,
+    launch_one<false, true>(h, w_dn, ybuf, h_scale, w_scale, at, s.F, s.H, s.K,
                             max_blocks, small, st, ksplit);
   else
-    launch_one<false, false>(h, w_dn, topk_w, ybuf, nullptr, nullptr, at, s.F, s.H, s.K,
+    launch_one<false, false>(h, w_dn, ybuf, nullptr, nullptr, at, s.F, s.H, s.K,
                              max_blocks, small, st, ksplit);
   return hipGetLastError();
 }

@@ -117,7 +117,7 @@ struct PipeMath<true> {    // FP8: one 128-deep step per stage, two 16-byte read
 template <bool GATE_UP, bool FP8>
 __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
-    const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
+    void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, int n_ctiles, const float* __restrict__ a_scale, const float* __restrict__ w_scale,
     int ksplit) {
   using M = PipeMath<FP8>;

@@ -52,7 +52,7 @@ struct SmallMath<true> {
 template <bool GATE_UP, bool FP8>
 __global__ __launch_bounds__(256) void grouped_small_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
-    const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
+    void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
   using M = SmallMath<FP8>;
   constexpr int U = kSmallBatchBytes / M::kStepBytes;   // MFMA steps per batch
@@ -154,7 +154,7 @@ struct KsBatch<true> {
 template <bool GATE_UP, bool FP8, int KSW>
 __global__ __launch_bounds__(64 * KSW) void grouped_small_ks_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
-    const float* __restrict__ topk_w, void* __restrict__ out, AlignTables at, int Kd, int Nout,
+    void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
   using M = SmallMath<FP8>;
   constexpr int U = KsBatch<FP8>::kBytes / M::kStepBytes;   // MFMA steps per batch
