@@ -47,6 +47,30 @@ def test_quant_fp8_bitwise_against_oracle():
     assert np.array_equal(c2.cpu().numpy(), w2c) and np.array_equal(s2.cpu().numpy(), w2s)
 
 
+@pytest.mark.parametrize("cols", [2560, 4096])
+def test_quant_fp8_many_rows_bitwise_sampled(cols):
+    """Prefill-sized row counts (16384 or more rows of up to 4096 values) take the quantiser that
+    runs one wave per row; its codes and scales on 256 sampled rows (first, last, special rows and
+    random ones) against the oracle, bit for bit."""
+    rng = np.random.default_rng(14)
+    n = 16384 + 37
+    x = rng.standard_normal((n, cols)) * (10.0 ** rng.uniform(-3, 3, size=(n, 1)))
+    x[5] = 0.0                                           # all-zero row
+    x[9, :] = 0.0
+    x[9, 3] = -0.0
+    x[9, 11] = 448.0                                     # amax exactly 448: scale 1
+    x[n - 1] *= 1e-30                                    # tiny amax, large inverse scale
+    xb = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+    _say("quantising", n, "rows of", cols)
+    codes, scales = bm.quant_fp8(xb.cuda())
+    torch.cuda.synchronize()
+    pick = np.unique(np.concatenate([[0, 5, 9, n - 2, n - 1], rng.choice(n, 251, replace=False)]))
+    want_c, want_s = codecs.quant_rows_fp8(xb[pick].float().numpy())
+    got_c, got_s = codes.cpu().numpy()[pick], scales.cpu().numpy()[pick]
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(got_c, want_c), np.argwhere(got_c != want_c)[:5]
+
+
 @pytest.fixture(scope="module")
 def beam_fp8():
     _say("generating Beam FP8 weights on cuda:0")
