@@ -25,8 +25,12 @@ namespace beam {
 // Per 16-wide K step a lane loads 4 consecutive K values of one token row (A) and of one expert
 // row (B); MFMA step c consumes component c, so step c sums K offsets {c, 4+c, 8+c, 12+c}: the same
 // permutation on both operands, hence the same products.
+// At most 128 VGPRs (four waves per SIMD, so a T=8192 grid of 1024 workgroups runs in one round
+// instead of 1.33): 0.275 -> 0.270 ms at T=8192, 1.06 -> 1.03 ms at T=32768. Loading the next
+// 16-deep step's operands ahead of the current MFMAs measured slower (0.35-0.40 ms), with or
+// without the cap.
 template <bool XBF16, int TM, int EB>
-__global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv,
+__global__ __launch_bounds__(256, 4) void router_logits_kernel(const void* __restrict__ xv,
                                                             const float* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             float2* __restrict__ sb, int64_t T,
