@@ -25,16 +25,14 @@ namespace beam {
 // Per 16-wide K step a lane loads 4 consecutive K values of one token row (A) and of one expert
 // row (B); MFMA step c consumes component c, so step c sums K offsets {c, 4+c, 8+c, 12+c}: the same
 // permutation on both operands, hence the same products.
-// At most 128 VGPRs (four waves per SIMD, so a T=8192 grid of 1024 workgroups runs in one round
-// instead of 1.33): 0.275 -> 0.270 ms at T=8192, 1.06 -> 1.03 ms at T=32768. Loading the next
-// 16-deep step's operands ahead of the current MFMAs measured slower (0.35-0.40 ms), with or
-// without the cap.
+// Tiles for T > 64: 64 tokens x 64 experts (each workgroup reads its 1.3 MB W_r slice for twice
+// as many tokens as with 32-token tiles: 0.275 -> 0.225 ms at T=8192, 1.03 -> 0.845 ms at
+// T=32768), two workgroups per CU by registers and LDS; 128-token tiles spill. Loading the next
+// 16-deep step's operands ahead of the current MFMAs measured slower.
 template <bool XBF16, int TM, int EB>
-__global__ __launch_bounds__(256, 4) void router_logits_kernel(const void* __restrict__ xv,
-                                                            const float* __restrict__ wr,
-                                                            const float* __restrict__ bias,
-                                                            float2* __restrict__ sb, int64_t T,
-                                                            int H, int E) {
+__global__ __launch_bounds__(256, TM >= 64 ? 2 : 4) void router_logits_kernel(
+    const void* __restrict__ xv, const float* __restrict__ wr, const float* __restrict__ bias,
+    float2* __restrict__ sb, int64_t T, int H, int E) {
   constexpr int MB = TM / 16, NB = EB / 16;
   __shared__ float part[4][TM][EB + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -196,12 +194,12 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_route
       hipLaunchKernelGGL((router_logits_kernel<false, 16, 16>), grid, dim3(256), 0, st, x,
                          w_router, bias, sb, s.T, s.H, s.E);
   } else {
-    dim3 grid((unsigned)ceil_div(s.T, 32), s.E / 64);
+    dim3 grid((unsigned)ceil_div(s.T, 64), s.E / 64);
     if (x_bf16)
-      hipLaunchKernelGGL((router_logits_kernel<true, 32, 64>), grid, dim3(256), 0, st, x,
+      hipLaunchKernelGGL((router_logits_kernel<true, 64, 64>), grid, dim3(256), 0, st, x,
                          w_router, bias, sb, s.T, s.H, s.E);
     else
-      hipLaunchKernelGGL((router_logits_kernel<false, 32, 64>), grid, dim3(256), 0, st, x,
+      hipLaunchKernelGGL((router_logits_kernel<false, 64, 64>), grid, dim3(256), 0, st, x,
                          w_router, bias, sb, s.T, s.H, s.E);
   }
   return hipGetLastError();
