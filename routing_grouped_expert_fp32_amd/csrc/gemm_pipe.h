@@ -207,11 +207,11 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Issue order: prologue A(0), B(0); iteration kt waits for everything it issued, passes the
-  // barrier (every wave's loads of stage kt have landed and every wave is done reading stage
-  // kt - 1, whose slots are reused), then issues A(kt+1), B(kt+1) and computes stage kt.
-  // epilogue operands of this tile: loads issued before the first stage's (FP8 gate/up: the token
-  // scale, which needs the slot id, behind them) and stored to LDS once they have landed
+  // Epilogue operands of this tile, staged in LDS after the rings: down: each row's slot id and
+  // routing weight (FP8: and its row scale); FP8: the tile's 256 output-channel scales; FP8
+  // gate/up: each row's token scale. Their loads go out before the first stage's (the token scale,
+  // which needs the slot id, right behind them); they are stored once they have landed.
+  static_assert(C::BM <= 64 * WAVES && kPBN <= 64 * WAVES, "one row / column per thread");
   int* const e_slot = reinterpret_cast<int*>(smem + C::kLdsBytes);
   float* const e_w = reinterpret_cast<float*>(smem + C::kLdsBytes + 4 * C::BM);
   float* const e_as = reinterpret_cast<float*>(smem + C::kLdsBytes + 8 * C::BM);
@@ -219,7 +219,6 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   int v_slot = 0;
   float v_w = 0.f, v_as = 0.f, v_ws = 0.f;
   if constexpr (!GATE_UP) {
-    static_assert(C::BM <= 64 * WAVES && kPBN <= 64 * WAVES, "one row / column per thread");
     if (tid < rows) {
       v_slot = at.sorted_slot[row0 + tid];
       v_w = at.sorted_w[row0 + tid];
@@ -230,16 +229,22 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   } else if constexpr (FP8) {   // tile columns: 128 gate channels, then the matching up channels
     if (tid < rows) v_slot = at.sorted_slot[row0 + tid];
     if (tid < kPBN)
-      v_ws = w_scale[(int64_t)e * 2 * Nout + (tid < 128 ? 128 * j + tid : Nout + 128 * j + tid - 128)];
+      v_ws = w_scale[(int64_t)e * 2 * Nout + (tid < 128 ? 0 : Nout - 128) + 128 * j + tid];
   }
+
+  // Issue order: prologue A(0), B(0); iteration kt waits for everything it issued, passes the
+  // barrier (every wave's loads of stage kt have landed and every wave is done reading stage
+  // kt - 1, whose slots are reused), then issues A(kt+1), B(kt+1) and computes stage kt.
   issue_a(0);
   issue_b(0);
   if constexpr (GATE_UP && FP8)
     if (tid < rows) v_as = a_scale[v_slot / topk];
   if constexpr (!GATE_UP || FP8) {
     if (tid < C::BM) {
-      e_slot[tid] = v_slot;
-      e_w[tid] = v_w;
+      if constexpr (!GATE_UP) {
+        e_slot[tid] = v_slot;
+        e_w[tid] = v_w;
+      }
       if constexpr (FP8) e_as[tid] = v_as;
     }
     if constexpr (FP8)
