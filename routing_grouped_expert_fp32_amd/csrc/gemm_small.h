@@ -133,11 +133,13 @@ __global__ __launch_bounds__(256) void grouped_small_kernel(
 // K-split variant: a WG covers 16 h columns (gate/up: each lane streams a gate row and the
 // matching up row) or 32 output columns (down: two 16-column groups, so a down workgroup streams as
 // many weight bytes as a gate/up one; measured 0.516 -> 0.503 ms at T=32), and its waves (4 or 8,
-// KSW) split K into equal parts (many more workgroups than the column-tiled kernel, which
-// matters when a handful of tokens touch few experts). Each wave keeps two batches of loads in
-// flight (the next batch is issued before the current one's MFMAs); the partial tiles are summed
-// in LDS in wave order (deterministic) and wave 0 runs the epilogue. Requires the rows' parts to
-// be whole batches.
+// KSW) split K (many more workgroups than the column-tiled kernel, which matters when a handful
+// of tokens touch few experts): wave w takes batches w, w + KSW, w + 2 KSW, ... of every row, so
+// at any moment a workgroup reads one contiguous stretch of each row (0.5-1.5% faster than
+// contiguous per-wave parts). Each wave keeps two batches of loads in flight (the next batch is
+// issued before the current one's MFMAs); the partial tiles are summed in LDS in wave order
+// (deterministic) and wave 0 runs the epilogue. Requires the rows to split into KSW x whole
+// batches.
 template <bool FP8>
 struct KsBatch {
   static constexpr int kBytes = 256;   // bf16: 4 steps of 64 B; FP8: 2 steps of 128 B
@@ -168,7 +170,8 @@ __global__ __launch_bounds__(64 * KSW) void grouped_small_ks_kernel(
   const int r = lane & 15, g = lane >> 4;
   const int c0 = blockIdx.x * (GATE_UP ? 16 : 32);
   const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
-  const int64_t kq = row_bytes / kKsWaves, kbeg = wave * kq;
+  constexpr int64_t BB = KsBatch<FP8>::kBytes;
+  const int64_t kq = row_bytes / kKsWaves, kbeg = wave * BB;   // batches wave, wave + KSW, ...
 
   const unsigned char* ap = nullptr;
   if (r < rows) {
@@ -206,14 +209,14 @@ __global__ __launch_bounds__(64 * KSW) void grouped_small_ks_kernel(
       acc1 = M::mma(a[buf][u], w1[buf][u], acc1);
     }
   };
-  constexpr int64_t BB = KsBatch<FP8>::kBytes;
   const int nb = (int)(kq / BB);
+  constexpr int64_t SB = BB * KSW;   // bytes between a wave's batches
   load(0, 0);
   int i = 0;
   for (; i + 2 <= nb; i += 2) {   // two batches per trip so the buffers stay in registers
-    load(1, (int64_t)(i + 1) * BB);
+    load(1, (int64_t)(i + 1) * SB);
     mma(0);
-    if (i + 2 < nb) load(0, (int64_t)(i + 2) * BB);
+    if (i + 2 < nb) load(0, (int64_t)(i + 2) * SB);
     mma(1);
   }
   if (i < nb) mma(0);   // odd count: batch nb-1 was loaded into buffer 0
