@@ -19,7 +19,7 @@ constexpr int kCombineMaxSlots = 16;   // top-k <= 16
 template <bool FILTER>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       void* __restrict__ out, int out_bf16,
-                                                      int64_t T, int H, int K,
+                                                      int H, int K,
                                                       const int32_t* __restrict__ ids, int e_begin,
                                                       int e_end) {
   const int64_t t = blockIdx.x;
@@ -67,10 +67,10 @@ hipError_t launch_combine(const float* ybuf, void* out, bool out_bf16, const Sha
   dim3 grid((unsigned)s.T, (unsigned)ceil_div(s.H, 1024));
   if (ids)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, st, ybuf, out, out_bf16 ? 1 : 0,
-                       s.T, s.H, s.K, ids, e_begin, e_end);
+                       s.H, s.K, ids, e_begin, e_end);
   else
     hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, st, ybuf, out, out_bf16 ? 1 : 0,
-                       s.T, s.H, s.K, ids, e_begin, e_end);
+                       s.H, s.K, ids, e_begin, e_end);
   return hipGetLastError();
 }
 
