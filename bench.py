@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
                     [--also prefill,skew,fp8_decode,fp8_prefill,routed_prefill,
-                            dense_prefill,boundary_prefill]
+                            dense_prefill,boundary_prefill,small_t]
                     [--no-cpu-baseline]
 
 A step is one beam_moe_forward over one batch (router, selection, moe_align, [FP8 quantisers],
@@ -20,7 +20,9 @@ beam_moe_forward_routed over one expert-parallel share (experts 32..63, one grou
 with the router's routes computed once beforehand; their bytes and FLOPs count the local slots and
 experts only. dense_prefill times beam_dense_mlp_forward on Beam's dense layer (d_ff 20480) at
 T=8192. boundary_prefill times beam_moe_forward_boundary (combine fused into the post-MoE
-norm -> residual -> norm boundary) and the standalone boundary at T=8192.
+norm -> residual -> norm boundary) and the standalone boundary at T=8192. small_t times the
+decode-shaped layer at T = 1, 2, 4, 8, 16 and 64 (no timing events inside the steps) against its HBM
+floor: distinct experts touched x 78.6 MB of bf16 weights / 8 TB/s.
 
 roofline (dominant kernel = the gate/up grouped GEMM). Algorithmic bytes per launch = distinct
 experts touched (counted from the routing of the batch) x the expert's gate and up weights (bf16:
@@ -72,7 +74,7 @@ def parse():
                    choices=["decode", "prefill", "skew", "fp8_decode", "fp8_prefill",
                             "routed_prefill", "routed_decode"])
     p.add_argument("--also", default="prefill,skew,fp8_decode,fp8_prefill,routed_prefill,"
-                   "dense_prefill,boundary_prefill",
+                   "dense_prefill,boundary_prefill,small_t",
                    help="comma list of extra workloads ('' = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ceilings", action="store_true",
@@ -432,6 +434,42 @@ def cpu_baseline(torch, synthgen, d, W, wl_name, n_tok):
     return res
 
 
+def measure_small_t(bm, synthgen, torch, weights, steps, warmup, Ts=(1, 2, 4, 8, 16, 64)):
+    """The decode-shaped layer at small token counts: ms per step (wall clock over `steps` calls,
+    no timing events), distinct experts touched, and the HBM floor of the weights they stream."""
+    wl = synthgen.WORKLOADS["decode"]
+    W = weights.get("bf16")
+    sh = wl.shape
+    cfg = bm.WorkloadCfg.of(sh, wl.x_dtype, wl.w_dtype)
+    stream = torch.cuda.current_stream()
+    per_expert = 3 * sh.d_ff * sh.hidden * 2   # gate, up and down rows, bf16
+    res = {}
+    for T in Ts:
+        d = synthgen.make_inputs(wl, device="cuda", T=T, with_experts=False)
+        ws = torch.empty(bm.workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+        out = torch.empty((T, sh.hidden), dtype=torch.float32, device="cuda")
+        ids = torch.empty((T, sh.topk), dtype=torch.int32, device="cuda")
+
+        def step():
+            bm.forward(d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg,
+                       out=out, topk_ids_out=ids, workspace=ws, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        distinct = int(torch.unique(ids).numel())
+        floor = distinct * per_expert / (HBM_PEAK_GBS * 1e9) * 1e3
+        res[str(T)] = {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+                       "distinct_experts": distinct, "hbm_floor_ms": floor,
+                       "frac_of_floor": floor / ms}
+    return res
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -456,6 +494,12 @@ def main():
             r = measure_boundary(bm, synthgen, torch, weights, max(5, a.steps // 5), a.warmup)
             extra[name] = r
             print(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+            continue
+        if name == "small_t":
+            r = measure_small_t(bm, synthgen, torch, weights, max(10, a.steps // 2), a.warmup)
+            extra[name] = r
+            print(f"[bench] {name}: " + ", ".join(f"T={t} {v['ms_per_step']:.3f} ms"
+                                                 for t, v in r.items()), file=sys.stderr, flush=True)
             continue
         if name == "dense_prefill":
             r = measure_dense(bm, synthgen, torch, 8192, max(5, a.steps // 5), a.warmup)
