@@ -228,6 +228,55 @@ BEAM_API beam_status_t beam_moe_forward_boundary(
 BEAM_API beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols,
                                           uint8_t* codes, float* scales, void* stream);
 
+/* Element conversion with the rounding routines of the kernels (the bf16 rounding points of the
+ * expert path, [S] §BF16 MoE Kernel Optimization; the E4M3 codes of the dynamic FP8 path, [S] §BF16,
+ * NVFP4 and FP8 Model Support), for checking them and for preparing inputs.
+ *   src  [n] fp32 (device); finite values
+ *   dst  [n] out: dst_dtype BEAM_BF16 -> bf16 bits rounded to nearest even (values past the largest
+ *        bf16 and NaN inputs are unspecified); BEAM_FP8_E4M3 -> OCP E4M3FN codes rounded to nearest
+ *        even and saturated to +-448, the sign of zero kept */
+BEAM_API beam_status_t beam_moe_convert(const float* src, int64_t n, int32_t dst_dtype, void* dst,
+                                        void* stream);
+
+/* Inspection of a forward's intermediate arrays, for tests and debugging. After a call of
+ * beam_moe_forward or beam_moe_forward_routed with the same cfg and T has completed on `workspace`,
+ * the bytes [*offset, *offset + *bytes) of that workspace hold the array named by `region`:
+ *   BEAM_WS_EXPERT_OFF  int32 [n + 1]  first sorted row of each of the call's n experts (n = E for
+ *                       beam_moe_forward, expert_end - expert_begin for the routed call); entry n
+ *                       is the number of sorted rows
+ *   BEAM_WS_SORTED_SLOT int32 [T*K]    slot t*K + k of each sorted row (rows of one expert are
+ *                       contiguous and in token order)
+ *   BEAM_WS_H           [T*K][F]       the expert activation h of each sorted row (bf16; fp32 for
+ *                       BEAM_F32 experts), after its rounding point
+ *   BEAM_WS_HQ, BEAM_WS_HS  (BEAM_FP8_E4M3 only) uint8 [T*K][F] E4M3 codes and fp32 [T*K] scales
+ *                       of the h rows, as the down GEMM consumes them
+ *   BEAM_WS_XQ, BEAM_WS_XS  (BEAM_FP8_E4M3 only) uint8 [T][H] E4M3 codes and fp32 [T] scales of x
+ *   BEAM_WS_Y           fp32 [T*K][H]  the weighted output topk_w * y of each slot (indexed by slot;
+ *                       slots routed outside the call's experts hold stale values)
+ * Rows past the number of sorted rows hold stale values. Returns BEAM_ERR_SHAPE / _UNSUPPORTED /
+ * _DTYPE as beam_moe_workspace_bytes would fail, BEAM_ERR_NULL for NULL outputs and
+ * BEAM_ERR_UNSUPPORTED for a region the cfg does not have (e.g. HQ without FP8 experts). No
+ * device work is done. */
+enum {
+  BEAM_WS_EXPERT_OFF = 0,
+  BEAM_WS_SORTED_SLOT = 1,
+  BEAM_WS_H = 2,
+  BEAM_WS_HQ = 3,
+  BEAM_WS_HS = 4,
+  BEAM_WS_XQ = 5,
+  BEAM_WS_XS = 6,
+  BEAM_WS_Y = 7
+};
+BEAM_API beam_status_t beam_moe_workspace_region(const beam_moe_cfg* cfg, int64_t T, int32_t region,
+                                                 size_t* offset, size_t* bytes);
+/* The same for a beam_dense_mlp_forward workspace (one expert that every token takes with weight 1:
+ * K = 1, n = 1). There BEAM_WS_Y is sized for up to four partial rows per token: a call whose down
+ * GEMM splits its K range into p parts writes row t*p + i with part i, summed in part order by the
+ * combine (p is chosen per call from the shape and the device and is not reported). */
+BEAM_API beam_status_t beam_dense_mlp_workspace_region(int32_t hidden, int32_t d_ff,
+                                                       int32_t w_dtype, int64_t T, int32_t region,
+                                                       size_t* offset, size_t* bytes);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 BEAM_API const char* beam_status_string(beam_status_t status);
 

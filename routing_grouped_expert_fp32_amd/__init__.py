@@ -22,7 +22,8 @@ __all__ = [
     "BEAM_F32", "BEAM_BF16", "BEAM_FP8_E4M3", "Cfg", "make_cfg", "lib", "lib_path", "route",
     "forward", "workspace_bytes", "route_workspace_bytes", "BeamError", "timing_enable",
     "timing_collect", "STAGES", "status_string", "quant_fp8", "forward_routed", "dense_mlp",
-    "dense_workspace_bytes", "residual_boundary", "forward_boundary",
+    "dense_workspace_bytes", "residual_boundary", "forward_boundary", "workspace_region",
+    "workspace_view", "WS_REGIONS", "convert", "dense_workspace_region",
 ]
 
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
@@ -107,6 +108,14 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward_boundary.restype = i32
         L.beam_moe_quant_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
         L.beam_moe_quant_fp8.restype = i32
+        L.beam_moe_workspace_region.argtypes = [cfgp, i64, i32, ctypes.POINTER(sz),
+                                                ctypes.POINTER(sz)]
+        L.beam_moe_workspace_region.restype = i32
+        L.beam_dense_mlp_workspace_region.argtypes = [i32, i32, i32, i64, i32,
+                                                      ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.beam_dense_mlp_workspace_region.restype = i32
+        L.beam_moe_convert.argtypes = [vp, i64, i32, vp, vp]
+        L.beam_moe_convert.restype = i32
         _LIB = L
     return _LIB
 
@@ -290,6 +299,55 @@ def quant_fp8(src, codes=None, scales=None, stream=None):
     if rc != 0:
         raise BeamError(rc, "beam_moe_quant_fp8")
     return codes, scales
+
+
+def convert(src, dst_dtype: int, dst=None, stream=None):
+    """beam_moe_convert: fp32 [n] -> bf16 (BEAM_BF16, returned as torch.bfloat16) or E4M3 codes
+    (BEAM_FP8_E4M3, returned as uint8) with the kernels' rounding routines."""
+    n = src.numel()
+    if dst is None:
+        dt = torch.bfloat16 if dst_dtype == BEAM_BF16 else torch.uint8
+        dst = torch.empty(src.shape, dtype=dt, device=src.device)
+    _check_dev(src, dst)
+    rc = lib().beam_moe_convert(_ptr(src), n, dst_dtype, _ptr(dst), _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_convert")
+    return dst
+
+
+WS_REGIONS = {"expert_off": 0, "sorted_slot": 1, "h": 2, "hq": 3, "hs": 4, "xq": 5, "xs": 6,
+              "y": 7}
+
+
+def workspace_region(cfg: Cfg, T: int, region: str) -> tuple:
+    """beam_moe_workspace_region: (byte offset, bytes) of an intermediate array in a forward's
+    workspace (names as in WS_REGIONS)."""
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    rc = lib().beam_moe_workspace_region(ctypes.byref(cfg), T, WS_REGIONS[region],
+                                         ctypes.byref(off), ctypes.byref(n))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_workspace_region")
+    return off.value, n.value
+
+
+def dense_workspace_region(hidden: int, d_ff: int, w_dtype: int, T: int, region: str) -> tuple:
+    """beam_dense_mlp_workspace_region: (byte offset, bytes) of an intermediate array."""
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    rc = lib().beam_dense_mlp_workspace_region(hidden, d_ff, w_dtype, T, WS_REGIONS[region],
+                                               ctypes.byref(off), ctypes.byref(n))
+    if rc != 0:
+        raise BeamError(rc, "beam_dense_mlp_workspace_region")
+    return off.value, n.value
+
+
+def workspace_view(workspace, cfg: Cfg, T: int, region: str, dtype, dense: bool = False):
+    """A flat torch view (no copy) of one intermediate array inside a forward's workspace (of
+    beam_dense_mlp_forward when dense is set; cfg then gives hidden, d_ff and w_dtype)."""
+    if dense:
+        off, n = dense_workspace_region(cfg.hidden, cfg.d_ff, cfg.w_dtype, T, region)
+    else:
+        off, n = workspace_region(cfg, T, region)
+    return workspace[off:off + n].view(dtype)
 
 
 def timing_enable(on: bool = True, stages=None) -> None:

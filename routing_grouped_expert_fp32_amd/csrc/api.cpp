@@ -86,13 +86,14 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full, int ybuf_parts =
     L.sorted_w = take(sizeof(float) * (size_t)TK);
     const size_t hel = c.w_dtype == BEAM_F32 ? 4 : 2;
     L.hbuf = take(hel * (size_t)TK * (size_t)c.d_ff);
-    L.ybuf = take(sizeof(float) * (size_t)TK * (size_t)ybuf_parts * (size_t)c.hidden);
     if (c.w_dtype == BEAM_FP8_E4M3) {
       L.xq = take((size_t)T * (size_t)c.hidden);
       L.xs = take(sizeof(float) * (size_t)T);
       L.hq = take((size_t)TK * (size_t)c.d_ff);
       L.hs = take(sizeof(float) * (size_t)TK);
     }
+    // last, so the offsets above do not depend on the number of partial rows per slot
+    L.ybuf = take(sizeof(float) * (size_t)TK * (size_t)ybuf_parts * (size_t)c.hidden);
   }
   L.total = off;
   return L;
@@ -360,6 +361,31 @@ int dense_ksplit_max(const beam_moe_cfg& c, int64_t T) {
   return m;
 }
 
+// Offset and size of one inspectable array of a forward's workspace (beam_moe_workspace_region).
+beam_status_t region_of(const beam_moe_cfg& c, const Layout& L, int64_t T, int y_parts,
+                        int32_t region, size_t* offset, size_t* bytes) {
+  const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
+  const size_t TK = (size_t)(T * c.topk), F = c.d_ff, H = c.hidden;
+  switch (region) {
+    case BEAM_WS_EXPERT_OFF: *offset = L.expert_off; *bytes = 4 * (size_t)(c.n_experts + 1); break;
+    case BEAM_WS_SORTED_SLOT: *offset = L.sorted; *bytes = 4 * TK; break;
+    case BEAM_WS_H: *offset = L.hbuf; *bytes = (c.w_dtype == BEAM_F32 ? 4 : 2) * TK * F; break;
+    case BEAM_WS_Y: *offset = L.ybuf; *bytes = 4 * TK * (size_t)y_parts * H; break;
+    case BEAM_WS_HQ:
+    case BEAM_WS_HS:
+    case BEAM_WS_XQ:
+    case BEAM_WS_XS:
+      if (!fp8) return BEAM_ERR_UNSUPPORTED;
+      if (region == BEAM_WS_HQ) { *offset = L.hq; *bytes = TK * F; }
+      if (region == BEAM_WS_HS) { *offset = L.hs; *bytes = 4 * TK; }
+      if (region == BEAM_WS_XQ) { *offset = L.xq; *bytes = (size_t)T * H; }
+      if (region == BEAM_WS_XS) { *offset = L.xs; *bytes = 4 * (size_t)T; }
+      break;
+    default: return BEAM_ERR_UNSUPPORTED;
+  }
+  return BEAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,6 +407,26 @@ const char* beam_status_string(beam_status_t s) {
 }
 
 int32_t beam_moe_version(void) { return 100; }
+
+beam_status_t beam_moe_workspace_region(const beam_moe_cfg* cfg, int64_t T, int32_t region,
+                                        size_t* offset, size_t* bytes) {
+  beam_status_t rc = check_cfg(cfg, true);
+  if (rc != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if (!offset || !bytes) return BEAM_ERR_NULL;
+  return region_of(*cfg, make_layout(*cfg, T, true), T, 1, region, offset, bytes);
+}
+
+beam_status_t beam_dense_mlp_workspace_region(int32_t hidden, int32_t d_ff, int32_t w_dtype,
+                                              int64_t T, int32_t region, size_t* offset,
+                                              size_t* bytes) {
+  beam_status_t rc = check_dense(hidden, d_ff, w_dtype, BEAM_F32, T);
+  if (rc != BEAM_OK) return rc;
+  if (!offset || !bytes) return BEAM_ERR_NULL;
+  const beam_moe_cfg c = dense_cfg(hidden, d_ff, w_dtype, BEAM_F32);
+  const int parts = dense_ksplit_max(c, T);
+  return region_of(c, make_layout(c, T, true, parts), T, parts, region, offset, bytes);
+}
 
 size_t beam_moe_route_workspace_bytes(const beam_moe_cfg* cfg, int64_t T) {
   if (check_cfg(cfg, false) != BEAM_OK || T < 0) return 0;
@@ -707,6 +753,23 @@ beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols, ui
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (beam::launch_quant_rows_fp8(reinterpret_cast<const uint16_t*>(src), rows, cols, codes, scales,
                                   st) != hipSuccess)
+    return BEAM_ERR_LAUNCH;
+  return BEAM_OK;
+}
+
+beam_status_t beam_moe_convert(const float* src, int64_t n, int32_t dst_dtype, void* dst,
+                               void* stream) {
+  if (n < 0) return BEAM_ERR_SHAPE;
+  if (dst_dtype != BEAM_BF16 && dst_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
+  if (n == 0) return BEAM_OK;
+  if (!src || !dst) return BEAM_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return BEAM_ERR_ALIGN;
+  const size_t nb = (size_t)n;
+  if (any_alias({rng(src, 4 * nb)}, {rng(dst, nb * dtype_bytes(dst_dtype))})) return BEAM_ERR_ALIAS;
+  beam_status_t rc = check_device();
+  if (rc != BEAM_OK) return rc;
+  if (beam::launch_convert(src, n, dst_dtype == BEAM_FP8_E4M3, dst,
+                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return BEAM_ERR_LAUNCH;
   return BEAM_OK;
 }

@@ -8,6 +8,8 @@
 //   code = E4M3(v * inv) rounded to nearest even and saturated to +-448; amax = 0 gives scale 1 and
 //   all-zero codes. The encoder is written out in integer arithmetic so the codes do not depend on
 //   any hardware conversion mode; the sign of zero follows the input (-0 -> 0x80).
+#include <algorithm>
+
 #include "common.h"
 
 namespace beam {
@@ -122,6 +124,36 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_wave_kernel(const uint16_t
     const int c = lane + 64 * i;
     if (c < n8) *reinterpret_cast<u32x2*>(o + 8 * c) = encode8(q[i], inv, zero);
   }
+}
+
+// Element conversions with the rounding routines the kernels use: fp32 -> bf16 (round to nearest
+// even) or fp32 -> E4M3 (round to nearest even, saturating), four elements per thread.
+template <bool TO_FP8>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ src, int64_t n,
+                                                      void* __restrict__ dst) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = i0; i < n; i += stride) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i + u >= n) break;
+      const float v = src[i + u];
+      if constexpr (TO_FP8)
+        reinterpret_cast<uint8_t*>(dst)[i + u] = (uint8_t)e4m3_rne_sat(v);
+      else
+        reinterpret_cast<uint16_t*>(dst)[i + u] = (uint16_t)f32_to_bf16_bits(v);
+    }
+  }
+}
+
+hipError_t launch_convert(const float* src, int64_t n, bool to_fp8, void* dst, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n, 1024), 65536);
+  if (to_fp8)
+    hipLaunchKernelGGL(convert_kernel<true>, dim3(grid), dim3(256), 0, st, src, n, dst);
+  else
+    hipLaunchKernelGGL(convert_kernel<false>, dim3(grid), dim3(256), 0, st, src, n, dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,

@@ -44,20 +44,44 @@ def test_small_dense_all_tokens(w_dtype, T, d_ff):
     at Beam's dense shape below)."""
     _say("dense small", w_dtype, T, d_ff)
     d = synthgen.make_dense(T, 512, d_ff, w_dtype, device="cuda", sigma_w=0.05)
+    if w_dtype == "fp8":
+        # one expert at a toy width: no combine averages the FP8 instructions' summation error over
+        # experts, and the end-to-end bar is held at the layer's real width below
+        # (test_beam_dense_fp8_every_token); every step is checked here against the GPU's own
+        # intermediate values within their bounds
+        stats, _ = _fp8_every_row(d, bar=False)
+        _say("toy dense FP8: max|err|/rms against the exact-sum oracle", stats["err_out_pure"])
+        return
     out = _run(d, w_dtype).cpu().numpy()
     ref = _oracle(d, w_dtype, np.arange(T))
     err, rms = parity.rel_err(out, ref)
-    p999 = float(np.quantile(np.abs(out - ref), 0.999) / rms)
-    _say("dense small", w_dtype, T, "max|err|/rms", err, "p99.9", p999)
-    if w_dtype == "fp8" and T * d["hidden"] > 64 * 512:
-        # Over many elements the FP8 bar meets its boundary flips: where the FP32 and FP64 paths
-        # put h (or its row amax) on different sides of a bf16 / E4M3 rounding boundary, an E4M3
-        # code moves by one step (6-12 %). Such flips are rare (median error ~5e-5) but their
-        # largest effect over ~3e5 outputs reaches ~5e-2; the tail is checked at the 99.9th
-        # percentile and the maximum at twice the bar.
-        assert p999 <= parity.FP8_P999 and err <= 2 * parity.TOL["fp8"]
-    else:
-        assert err <= parity.TOL[w_dtype]
+    _say("dense small", w_dtype, T, "max|err|/rms", err)
+    assert err <= parity.TOL[w_dtype]
+
+
+def _fp8_every_row(d, bar=True):
+    """FP8 dense layer through the every-row check (fullcheck.py): the layer is one expert that
+    every token takes with weight 1, so the MoE rules apply with E = K = 1. bar: also hold every
+    token other than the counted near-flip tokens to the FP8 bar against the pure oracle."""
+    import fullcheck
+    T, H, F = d["T"], d["hidden"], d["d_ff"]
+    cfg = bm.make_cfg(H, 1, 1, 1, 1, F, 1.0, bm.BEAM_BF16, bm.BEAM_FP8_E4M3, bm.BEAM_F32)
+    ws = torch.empty(bm.dense_workspace_bytes(H, F, bm.BEAM_FP8_E4M3, T), dtype=torch.uint8,
+                     device="cuda")
+    out = bm.dense_mlp(d["x"], d["w_gate_up"], d["w_down"], w_gate_up_scale=d["w_gate_up_scale"],
+                       w_down_scale=d["w_down_scale"], workspace=ws)
+    torch.cuda.synchronize()
+    ex = fullcheck.expert_f64(d["w_gate_up"], d["w_down"], F, d["w_gate_up_scale"],
+                              d["w_down_scale"])
+    st = fullcheck.read_state(ws, cfg, T, True, dense=True)
+    parts = st["y"].numel() // (T * H)
+    stats = fullcheck.check_batch(out, d["x"], np.zeros((T, 1), dtype=np.int64), np.ones((T, 1)),
+                                  st, lambda e: ex, "fp8", 1, say=_say, y_parts=parts)
+    assert stats["tokens_checked"] == T
+    assert stats["near_flip_tokens"] <= max(2, T // 50), stats
+    if bar:
+        assert stats["err_out_pure"] <= parity.TOL["fp8"], stats
+    return stats, parts
 
 
 @pytest.fixture(scope="module")
@@ -92,22 +116,17 @@ def test_beam_dense_decode_all_tokens(beam_dense):
     assert err <= parity.TOL["bf16"]
 
 
-def test_beam_dense_fp8_sampled():
-    """Beam's dense layer with FP8 weights at T = 8192 (the down GEMM splits K into 4 parts),
-    sampled tokens against the oracle's FP8 contract; and at T = 32 every token."""
+def test_beam_dense_fp8_every_token():
+    """Beam's dense layer with FP8 weights (5120 x 20480): every token of a 2048-token batch (the
+    down GEMM splits K into 4 parts) through the every-row check, at the FP8 bar against the pure
+    oracle except counted near-flip tokens; and T = 32 (decode kernels) likewise."""
     _say("generating Beam dense layer (5120 x 20480, FP8) on cuda:0")
-    d = synthgen.make_dense(8192, w_dtype="fp8", device="cuda")
+    d = synthgen.make_dense(2048, w_dtype="fp8", device="cuda")
     torch.cuda.synchronize()
-    out = _run(d, "fp8")
-    toks = np.array([0, 1, 777, 4095, 6000, 8191])
-    ref = _oracle(d, "fp8", toks)
-    err, rms = parity.rel_err(out[torch.from_numpy(toks).cuda()].cpu().numpy(), ref)
-    _say("Beam dense FP8 T=8192 sampled max|err|/rms", err)
-    assert err <= parity.TOL["fp8"]
+    stats, parts = _fp8_every_row(d)
+    _say("Beam dense FP8 T=2048, down K parts", parts, stats)
+    assert parts == 4
     d32 = dict(d)
     d32["x"] = d["x"][:32].contiguous()
     d32["T"] = 32
-    out = _run(d32, "fp8").cpu().numpy()
-    err, rms = parity.rel_err(out, _oracle(d32, "fp8", np.arange(32)))
-    _say("Beam dense FP8 T=32 max|err|/rms", err)
-    assert err <= parity.TOL["fp8"]
+    _fp8_every_row(d32)
