@@ -238,6 +238,15 @@ BEAM_API beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t
 BEAM_API beam_status_t beam_moe_convert(const float* src, int64_t n, int32_t dst_dtype, void* dst,
                                         void* stream);
 
+/* The FP8 matrix instruction of the FP8 expert GEMMs on caller tiles, for checking its summation:
+ * per tile t, d[t] = a[t] . b[t]^T + c[t] with one 16x16x128 E4M3 MFMA (unit block scales), the sum
+ * taken by the instruction itself (it does not round each partial sum to FP32: its result can differ
+ * from the FP32 rounding of the exact sum by a few 1e-4 of the largest |product|).
+ *   a, b  [n_tiles][16][128] uint8 E4M3 codes (rows along the 128-deep contraction)
+ *   c, d  [n_tiles][16][16] fp32 (d[t][i][j] = sum_k a[t][i][k] b[t][j][k] + c[t][i][j]) */
+BEAM_API beam_status_t beam_moe_fp8_dot_tiles(const uint8_t* a, const uint8_t* b, const float* c,
+                                              float* d, int64_t n_tiles, void* stream);
+
 /* Inspection of a forward's intermediate arrays, for tests and debugging. After a call of
  * beam_moe_forward or beam_moe_forward_routed with the same cfg and T has completed on `workspace`,
  * the bytes [*offset, *offset + *bytes) of that workspace hold the array named by `region`:

@@ -23,7 +23,7 @@ __all__ = [
     "forward", "workspace_bytes", "route_workspace_bytes", "BeamError", "timing_enable",
     "timing_collect", "STAGES", "status_string", "quant_fp8", "forward_routed", "dense_mlp",
     "dense_workspace_bytes", "residual_boundary", "forward_boundary", "workspace_region",
-    "workspace_view", "WS_REGIONS", "convert", "dense_workspace_region",
+    "workspace_view", "WS_REGIONS", "convert", "dense_workspace_region", "fp8_dot_tiles",
 ]
 
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
@@ -114,6 +114,8 @@ def lib() -> ctypes.CDLL:
         L.beam_dense_mlp_workspace_region.argtypes = [i32, i32, i32, i64, i32,
                                                       ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.beam_dense_mlp_workspace_region.restype = i32
+        L.beam_moe_fp8_dot_tiles.argtypes = [vp, vp, vp, vp, i64, vp]
+        L.beam_moe_fp8_dot_tiles.restype = i32
         L.beam_moe_convert.argtypes = [vp, i64, i32, vp, vp]
         L.beam_moe_convert.restype = i32
         _LIB = L
@@ -313,6 +315,17 @@ def convert(src, dst_dtype: int, dst=None, stream=None):
     if rc != 0:
         raise BeamError(rc, "beam_moe_convert")
     return dst
+
+
+def fp8_dot_tiles(a, b, c, stream=None):
+    """beam_moe_fp8_dot_tiles on uint8 codes a, b [n][16][128] and fp32 c [n][16][16]: returns d."""
+    d = torch.empty_like(c)
+    _check_dev(a, b, c, d)
+    rc = lib().beam_moe_fp8_dot_tiles(_ptr(a), _ptr(b), _ptr(c), _ptr(d), a.shape[0],
+                                      _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_fp8_dot_tiles")
+    return d
 
 
 WS_REGIONS = {"expert_off": 0, "sorted_slot": 1, "h": 2, "hq": 3, "hs": 4, "xq": 5, "xs": 6,

@@ -361,6 +361,65 @@ int dense_ksplit_max(const beam_moe_cfg& c, int64_t T) {
   return m;
 }
 
+// beam_moe_forward on a given workspace (also the no-allocation entry point's body).
+beam_status_t forward_impl(const void* x, const float* w_router, const float* bias,
+                           const void* w_gate_up, const void* w_down, void* out, int64_t T,
+                           const beam_moe_cfg* cfg, const float* w_gate_up_scale,
+                           const float* w_down_scale, int32_t* topk_ids_out, float* topk_w_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  beam_status_t rc = check_cfg(cfg, true);
+  if (rc != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  const beam_moe_cfg& c = *cfg;
+  const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
+  if (!fp8 && (w_gate_up_scale || w_down_scale)) return BEAM_ERR_DTYPE;
+  if (T == 0) return BEAM_OK;
+  if (!x || !w_router || !bias || !w_gate_up || !w_down || !out || !workspace) return BEAM_ERR_NULL;
+  if (fp8 && (!w_gate_up_scale || !w_down_scale)) return BEAM_ERR_NULL;
+  const void* ptrs[] = {x, w_router, bias, w_gate_up, w_down, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BEAM_ERR_ALIGN;
+  if ((topk_ids_out && !aligned16(topk_ids_out)) || (topk_w_out && !aligned16(topk_w_out)) ||
+      (w_gate_up_scale && !aligned16(w_gate_up_scale)) || (w_down_scale && !aligned16(w_down_scale)))
+    return BEAM_ERR_ALIGN;
+  const Layout L = make_layout(c, T, true);
+  if (L.max_blocks > 65535) return BEAM_ERR_UNSUPPORTED;   // grid.y bound of the GEMM launches
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+
+  const size_t H = c.hidden, E = c.n_experts, F = c.d_ff, TK = (size_t)(T * c.topk);
+  const size_t wb = dtype_bytes(c.w_dtype);
+  std::vector<Range> ins = {rng(x, (size_t)T * H * dtype_bytes(c.x_dtype)),
+                            rng(w_router, sizeof(float) * E * H), rng(bias, sizeof(float) * E),
+                            rng(w_gate_up, wb * E * 2 * F * H), rng(w_down, wb * E * H * F)};
+  if (fp8) {
+    ins.push_back(rng(w_gate_up_scale, sizeof(float) * E * 2 * F));
+    ins.push_back(rng(w_down_scale, sizeof(float) * E * H));
+  }
+  std::vector<Range> outs = {rng(out, (size_t)T * H * dtype_bytes(c.out_dtype)),
+                             rng(workspace, L.total)};
+  if (topk_ids_out) outs.push_back(rng(topk_ids_out, sizeof(int32_t) * TK));
+  if (topk_w_out) outs.push_back(rng(topk_w_out, sizeof(float) * TK));
+  if (any_alias(ins, outs)) return BEAM_ERR_ALIAS;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  const beam::Shape s = shape_of(c, T);
+  if (beam::use_small_route(s)) {   // partial logits, selection summing them
+    float* part = reinterpret_cast<float*>(ws + L.sb);
+    LAUNCH(0, beam::launch_router_partials(x, c.x_dtype == BEAM_BF16, w_router, part, s, st));
+    LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
+  } else {
+    LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
+    LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  }
+  return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
+                     out, 0, c.n_experts, false, st);
+}
+
 // Offset and size of one inspectable array of a forward's workspace (beam_moe_workspace_region).
 beam_status_t region_of(const beam_moe_cfg& c, const Layout& L, int64_t T, int y_parts,
                         int32_t region, size_t* offset, size_t* bytes) {
@@ -483,57 +542,8 @@ beam_status_t beam_moe_forward(const void* x, const float* w_router, const float
                                const float* w_down_scale, int32_t* topk_ids_out,
                                float* topk_w_out, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  beam_status_t rc = check_cfg(cfg, true);
-  if (rc != BEAM_OK) return rc;
-  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
-  const beam_moe_cfg& c = *cfg;
-  const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
-  if (!fp8 && (w_gate_up_scale || w_down_scale)) return BEAM_ERR_DTYPE;
-  if (T == 0) return BEAM_OK;
-  if (!x || !w_router || !bias || !w_gate_up || !w_down || !out || !workspace) return BEAM_ERR_NULL;
-  if (fp8 && (!w_gate_up_scale || !w_down_scale)) return BEAM_ERR_NULL;
-  const void* ptrs[] = {x, w_router, bias, w_gate_up, w_down, out, workspace};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return BEAM_ERR_ALIGN;
-  if ((topk_ids_out && !aligned16(topk_ids_out)) || (topk_w_out && !aligned16(topk_w_out)) ||
-      (w_gate_up_scale && !aligned16(w_gate_up_scale)) || (w_down_scale && !aligned16(w_down_scale)))
-    return BEAM_ERR_ALIGN;
-  const Layout L = make_layout(c, T, true);
-  if (L.max_blocks > 65535) return BEAM_ERR_UNSUPPORTED;   // grid.y bound of the GEMM launches
-  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
-
-  const size_t H = c.hidden, E = c.n_experts, F = c.d_ff, TK = (size_t)(T * c.topk);
-  const size_t wb = dtype_bytes(c.w_dtype);
-  std::vector<Range> ins = {rng(x, (size_t)T * H * dtype_bytes(c.x_dtype)),
-                            rng(w_router, sizeof(float) * E * H), rng(bias, sizeof(float) * E),
-                            rng(w_gate_up, wb * E * 2 * F * H), rng(w_down, wb * E * H * F)};
-  if (fp8) {
-    ins.push_back(rng(w_gate_up_scale, sizeof(float) * E * 2 * F));
-    ins.push_back(rng(w_down_scale, sizeof(float) * E * H));
-  }
-  std::vector<Range> outs = {rng(out, (size_t)T * H * dtype_bytes(c.out_dtype)),
-                             rng(workspace, L.total)};
-  if (topk_ids_out) outs.push_back(rng(topk_ids_out, sizeof(int32_t) * TK));
-  if (topk_w_out) outs.push_back(rng(topk_w_out, sizeof(float) * TK));
-  if (any_alias(ins, outs)) return BEAM_ERR_ALIAS;
-  if ((rc = check_device()) != BEAM_OK) return rc;
-
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* ws = reinterpret_cast<char*>(workspace);
-  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
-  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
-  float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  const beam::Shape s = shape_of(c, T);
-  if (beam::use_small_route(s)) {   // partial logits, selection summing them
-    float* part = reinterpret_cast<float*>(ws + L.sb);
-    LAUNCH(0, beam::launch_router_partials(x, c.x_dtype == BEAM_BF16, w_router, part, s, st));
-    LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
-  } else {
-    LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
-    LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
-  }
-  return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
-                     out, 0, c.n_experts, false, st);
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, out, T, cfg, w_gate_up_scale,
+                      w_down_scale, topk_ids_out, topk_w_out, workspace, workspace_bytes, stream);
 }
 
 beam_status_t beam_residual_boundary(const void* y, int32_t y_dtype, const void* h,
@@ -770,6 +780,24 @@ beam_status_t beam_moe_convert(const float* src, int64_t n, int32_t dst_dtype, v
   if (rc != BEAM_OK) return rc;
   if (beam::launch_convert(src, n, dst_dtype == BEAM_FP8_E4M3, dst,
                            reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return BEAM_ERR_LAUNCH;
+  return BEAM_OK;
+}
+
+beam_status_t beam_moe_fp8_dot_tiles(const uint8_t* a, const uint8_t* b, const float* c, float* d,
+                                     int64_t n_tiles, void* stream) {
+  if (n_tiles < 0) return BEAM_ERR_SHAPE;
+  if (n_tiles >= (int64_t(1) << 31)) return BEAM_ERR_UNSUPPORTED;
+  if (n_tiles == 0) return BEAM_OK;
+  if (!a || !b || !c || !d) return BEAM_ERR_NULL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c) || !aligned16(d)) return BEAM_ERR_ALIGN;
+  const size_t n = (size_t)n_tiles;
+  if (any_alias({rng(a, 2048 * n), rng(b, 2048 * n), rng(c, 1024 * n)}, {rng(d, 1024 * n)}))
+    return BEAM_ERR_ALIAS;
+  beam_status_t rc = check_device();
+  if (rc != BEAM_OK) return rc;
+  if (beam::launch_fp8_dot_tiles(a, b, c, d, n_tiles, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return BEAM_ERR_LAUNCH;
   return BEAM_OK;
 }

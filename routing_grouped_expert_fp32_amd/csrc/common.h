@@ -111,6 +111,8 @@ hipError_t launch_down_f32(const float* hbuf, const float* w_dn, const float* to
 hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
                                  float* scales, hipStream_t st);
 hipError_t launch_convert(const float* src, int64_t n, bool to_fp8, void* dst, hipStream_t st);
+hipError_t launch_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, const float* C, float* D,
+                                int64_t n, hipStream_t st);
 int small_block_rows();
 int tiled_block_rows(bool fp8);   // rows per block of the tiled GEMMs
 // post-norm -> depth-scaled residual -> next pre-norm (boundary.hip)

@@ -146,6 +146,36 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
   }
 }
 
+// One 16x16x128 E4M3 MFMA per tile (the instruction of the FP8 expert GEMMs, unit block scales):
+// D = A B^T + C for A [16][128] and B [16][128] codes (each row along K) and C, D [16][16] FP32.
+__global__ __launch_bounds__(64) void fp8_dot_tile_kernel(const uint8_t* __restrict__ A,
+                                                          const uint8_t* __restrict__ B,
+                                                          const float* __restrict__ C,
+                                                          float* __restrict__ D, int64_t n) {
+  const int64_t t = blockIdx.x;
+  if (t >= n) return;
+  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  const uint8_t* a = A + t * 2048 + r * 128 + 32 * g;
+  const uint8_t* b = B + t * 2048 + r * 128 + 32 * g;
+  const intx4 a0 = *reinterpret_cast<const intx4*>(a), a1 = *reinterpret_cast<const intx4*>(a + 16);
+  const intx4 b0 = *reinterpret_cast<const intx4*>(b), b1 = *reinterpret_cast<const intx4*>(b + 16);
+  const intx8 av = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const intx8 bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  floatx4 c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = C[t * 256 + (4 * g + i) * 16 + r];
+  const floatx4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) D[t * 256 + (4 * g + i) * 16 + r] = d[i];
+}
+
+hipError_t launch_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, const float* C, float* D,
+                                int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_dot_tile_kernel, dim3((unsigned)n), dim3(64), 0, st, A, B, C, D, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_convert(const float* src, int64_t n, bool to_fp8, void* dst, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n, 1024), 65536);

@@ -214,3 +214,45 @@ def test_e4m3_rounding_exhaustive():
     big = np.concatenate([big, big | np.uint32(1 << 31)])
     assert np.array_equal(_gpu_convert(big, bm.BEAM_FP8_E4M3), oracle_codes(big))
     _say("E4M3 encoder: fp32 values checked", n_checked + len(big))
+
+
+def test_fp8_instruction_summation_bound():
+    """The bound the every-row FP8 checks assume for the FP8 matrix instruction (fullcheck.FP8_BLOCK_
+    REL): each 16x16x128 E4M3 MFMA result lies within 2^-10 of its largest |product| of the exact
+    sum (with the accumulator input added). Random finite codes over the whole range, codes of the
+    magnitudes the kernels see (activations and weights scaled to +-448), and planted tiles with one
+    large product among many small ones; exact sums in float64 on the host. Also shows that the
+    instruction does not simply return the FP32 rounding of the exact sum."""
+    import fullcheck
+    rng = np.random.default_rng(11)
+    lut = fullcheck.LUT_E4M3
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    scaled = np.array([c for c in finite if 6 <= (c >> 3) & 15 <= 14], dtype=np.uint8)
+    n = 2048
+    worst, n_fp32_exact, total = 0.0, 0, 0
+    for kind in ("all", "scaled", "planted", "scaled+c"):
+        pool = finite if kind == "all" else scaled
+        a = rng.choice(pool, size=(n, 16, 128))
+        b = rng.choice(pool, size=(n, 16, 128))
+        c = np.zeros((n, 16, 16), dtype=np.float32)
+        if kind == "planted":
+            a[:] = 0x38
+            b[:] = 0x38                                       # 1.0 x 1.0 everywhere ...
+            k = rng.integers(0, 128, size=n)
+            a[np.arange(n), :, k] = (7 + rng.integers(0, 9, size=(n, 16))) << 3   # ... but one 2^j
+            b[np.arange(n), :, k] = (7 + rng.integers(0, 9, size=(n, 16))) << 3
+        if kind == "scaled+c":
+            c = rng.uniform(-1e6, 1e6, size=(n, 16, 16)).astype(np.float32)
+        d = fp_tiles = bm.fp8_dot_tiles(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(),
+                                        torch.from_numpy(c).cuda()).cpu().numpy().astype(np.float64)
+        del fp_tiles
+        av, bv = lut[a], lut[b]
+        exact = np.einsum("tik,tjk->tij", av, bv) + c
+        maxp = np.max(np.abs(av)[:, :, None, :] * np.abs(bv)[:, None, :, :], axis=3)
+        worst = max(worst, float(np.max(np.abs(d - exact) / maxp)))
+        n_fp32_exact += int(np.sum(d == exact.astype(np.float32)))
+        total += d.size
+    _say("FP8 MFMA: worst |error| / largest |product|", worst, "; results equal to the FP32 rounding",
+         "of the exact sum:", n_fp32_exact, "of", total)
+    assert worst <= fullcheck.FP8_BLOCK_REL
+    assert n_fp32_exact < total
