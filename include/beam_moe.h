@@ -129,6 +129,24 @@ BEAM_API beam_status_t beam_moe_forward(const void* x, const float* w_router, co
                                void* stream);
 BEAM_API size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int64_t T);
 
+/* beam_moe_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
+ * workspace is a 64 MiB array of device memory the library holds per GPU until the process ends
+ * (enough for beam_moe_workspace_bytes(cfg, T) <= 64 MiB: Beam's shape up to 324 tokens with bf16
+ * experts, 288 with FP8 ones). The call
+ * itself allocates nothing and leaves no state that a later call depends on.
+ *   Arguments and results as for beam_moe_forward, without workspace / workspace_bytes.
+ *   BEAM_ERR_WORKSPACE: beam_moe_workspace_bytes(cfg, T) exceeds 64 MiB (nothing is launched).
+ * Every call on one GPU uses that GPU's one array: calls that may overlap on one GPU (different
+ * streams, host threads) race and must be ordered by the caller. */
+BEAM_API beam_status_t beam_moe_forward_noalloc(const void* x, const float* w_router,
+                                                const float* bias, const void* w_gate_up,
+                                                const void* w_down, void* out, int64_t T,
+                                                const beam_moe_cfg* cfg,
+                                                const float* w_gate_up_scale,
+                                                const float* w_down_scale, int32_t* topk_ids_out,
+                                                float* topk_w_out, void* stream);
+
 /* Steps 4-5 with given routes, over a range of experts (routing replay and the expert-parallel
  * entry point: the routes are recorded once and reused instead of recomputed, so near-tied router
  * scores cannot pick a different expert path, [S] §Reinforcement learning in Miles; an expert-

@@ -24,6 +24,7 @@ __all__ = [
     "timing_collect", "STAGES", "status_string", "quant_fp8", "forward_routed", "dense_mlp",
     "dense_workspace_bytes", "residual_boundary", "forward_boundary", "workspace_region",
     "workspace_view", "WS_REGIONS", "convert", "dense_workspace_region", "fp8_dot_tiles",
+    "forward_noalloc",
 ]
 
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
@@ -114,6 +115,9 @@ def lib() -> ctypes.CDLL:
         L.beam_dense_mlp_workspace_region.argtypes = [i32, i32, i32, i64, i32,
                                                       ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.beam_dense_mlp_workspace_region.restype = i32
+        L.beam_moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, cfgp, vp, vp, vp, vp,
+                                               vp]
+        L.beam_moe_forward_noalloc.restype = i32
         L.beam_moe_fp8_dot_tiles.argtypes = [vp, vp, vp, vp, i64, vp]
         L.beam_moe_fp8_dot_tiles.restype = i32
         L.beam_moe_convert.argtypes = [vp, i64, i32, vp, vp]
@@ -191,6 +195,24 @@ def forward(x, w_router, bias, w_gate_up, w_down, cfg: Cfg, out=None, w_gate_up_
                                 _stream(stream))
     if rc != 0:
         raise BeamError(rc, "beam_moe_forward")
+    return out
+
+
+def forward_noalloc(x, w_router, bias, w_gate_up, w_down, cfg: Cfg, out=None, w_gate_up_scale=None,
+                    w_down_scale=None, topk_ids_out=None, topk_w_out=None, stream=None):
+    """beam_moe_forward_noalloc: beam_moe_forward on the library's own per-GPU workspace."""
+    T = x.shape[0]
+    if out is None:
+        odt = torch.bfloat16 if cfg.out_dtype == BEAM_BF16 else torch.float32
+        out = torch.empty((T, cfg.hidden), dtype=odt, device=x.device)
+    _check_dev(x, w_router, bias, w_gate_up, w_down, out, w_gate_up_scale, w_down_scale,
+               topk_ids_out, topk_w_out)
+    rc = lib().beam_moe_forward_noalloc(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up),
+                                        _ptr(w_down), _ptr(out), T, ctypes.byref(cfg),
+                                        _ptr(w_gate_up_scale), _ptr(w_down_scale),
+                                        _ptr(topk_ids_out), _ptr(topk_w_out), _stream(stream))
+    if rc != 0:
+        raise BeamError(rc, "beam_moe_forward_noalloc")
     return out
 
 

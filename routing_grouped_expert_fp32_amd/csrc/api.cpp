@@ -420,6 +420,28 @@ beam_status_t forward_impl(const void* x, const float* w_router, const float* bi
                      out, 0, c.n_experts, false, st);
 }
 
+// Workspace of the no-allocation entry point: one array per GPU, in device memory the library holds
+// until the process ends. In host code `scratch` names a host-side stand-in, not the device array:
+// the device address comes from hipGetSymbolAddress, once per device with that device current,
+// and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+beam_status_t scratch_of_current_device(void** out) {
+  static void* ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BEAM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_ERR_DEVICE;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return BEAM_OK;
+}
+
 // Offset and size of one inspectable array of a forward's workspace (beam_moe_workspace_region).
 beam_status_t region_of(const beam_moe_cfg& c, const Layout& L, int64_t T, int y_parts,
                         int32_t region, size_t* offset, size_t* bytes) {
@@ -544,6 +566,23 @@ beam_status_t beam_moe_forward(const void* x, const float* w_router, const float
                                void* stream) {
   return forward_impl(x, w_router, bias, w_gate_up, w_down, out, T, cfg, w_gate_up_scale,
                       w_down_scale, topk_ids_out, topk_w_out, workspace, workspace_bytes, stream);
+}
+
+beam_status_t beam_moe_forward_noalloc(const void* x, const float* w_router, const float* bias,
+                                       const void* w_gate_up, const void* w_down, void* out,
+                                       int64_t T, const beam_moe_cfg* cfg,
+                                       const float* w_gate_up_scale, const float* w_down_scale,
+                                       int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  beam_status_t rc = check_cfg(cfg, true);
+  if (rc != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if (T == 0) return BEAM_OK;
+  if (make_layout(*cfg, T, true).total > kScratchBytes) return BEAM_ERR_WORKSPACE;
+  if ((rc = check_device()) != BEAM_OK) return rc;
+  void* scratch_ptr = nullptr;
+  if ((rc = scratch_of_current_device(&scratch_ptr)) != BEAM_OK) return rc;
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, out, T, cfg, w_gate_up_scale,
+                      w_down_scale, topk_ids_out, topk_w_out, scratch_ptr, kScratchBytes, stream);
 }
 
 beam_status_t beam_residual_boundary(const void* y, int32_t y_dtype, const void* h,
