@@ -316,7 +316,8 @@ BEAM_API int32_t beam_moe_version(void);
  * totals (milliseconds) and launch counts for up to n_stages stages, releases the events and
  * returns the number of stages defined. Stage order: 0 router logits, 1 router select,
  * 2 moe_align, 3 activation quant (fp8), 4 gate/up GEMM, 5 h quant (fp8), 6 down GEMM,
- * 7 combine. beam_moe_stage_name(i) names stage i.
+ * 7 combine (for forwards of up to 16 tokens the selection and the align are one launch, recorded
+ * as stage 1). beam_moe_stage_name(i) names stage i.
  * beam_moe_timing_stages(mask) restricts the recording to the stages whose bit (1 << stage) is set
  * (default: all), so a caller can time one kernel without event records between the others. */
 BEAM_API void beam_moe_timing_enable(int32_t enable);

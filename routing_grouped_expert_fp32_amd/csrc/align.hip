@@ -20,6 +20,7 @@
 // Slots of one token name distinct experts (the router guarantees it; for given routes a repeated
 // id within a token leaves one of its slots out, which is memory-safe).
 #include "common.h"
+#include "route_select.h"
 
 namespace beam {
 
@@ -251,6 +252,48 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __rest
                                                            AlignTables at, int64_t T, int E, int K,
                                                            int e_begin, int BM) {
   align_small_body(ids, tw, T, E, K, e_begin, BM, at);
+}
+
+// The smallest batches of the forward (up to 16 tokens): selection and align in one launch. One
+// workgroup of 16 waves: wave w selects token w (select_token), writes its routes and keeps them in
+// LDS, then the workgroup groups the slots by expert (align_small_body) from LDS. (With more tokens
+// a single workgroup would select several tokens per wave one after another, slower than the
+// selection over many workgroups plus a separate align launch.)
+__global__ __launch_bounds__(1024) void select_align_small_kernel(ScoresFromPartials src,
+                                                                  int32_t* __restrict__ ids,
+                                                                  float* __restrict__ wout,
+                                                                  AlignTables at, int64_t T, int E,
+                                                                  int G, int Gk, int K, float scale,
+                                                                  int BM) {
+  __shared__ float bl[16][256];
+  __shared__ float gsc[16][64];
+  __shared__ int32_t sid[kSmallRouteT * 16];
+  __shared__ float sw[kSmallRouteT * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t t = wave; t < T; t += 16) {
+    int id;
+    float w;
+    select_token(src, t, lane, bl[wave], gsc[wave], E, G, Gk, K, scale, id, w);
+    if (lane < K) {
+      ids[t * K + lane] = id;
+      wout[t * K + lane] = w;
+      sid[t * K + lane] = id;
+      sw[t * K + lane] = w;
+    }
+  }
+  __syncthreads();
+  align_small_body(sid, sw, T, E, K, 0, BM, at);
+}
+
+hipError_t launch_select_align_small(const float* part, const float* bias, int32_t* ids, float* w,
+                                     const AlignTables& at, const Shape& s, int BM,
+                                     hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (!use_fused_select_align(s)) return hipErrorInvalidValue;
+  const ScoresFromPartials src{part, bias, router_partial_chunks(s), s.T, s.E};
+  hipLaunchKernelGGL(select_align_small_kernel, dim3(1), dim3(1024), 0, st, src, ids, w, at, s.T,
+                     s.E, s.G, s.Gk, s.K, s.scale, BM);
+  return hipGetLastError();
 }
 
 // Routes of a dense layer run as one expert: every token's single slot goes to expert 0 with

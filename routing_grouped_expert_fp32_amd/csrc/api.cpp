@@ -245,7 +245,8 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
                           const void* w_gate_up, const void* w_down,
                           const float* w_gate_up_scale, const float* w_down_scale, void* out,
                           int e_begin, int e_count, bool filter, hipStream_t st,
-                          const beam::BoundaryArgs* bnd = nullptr, int ksplit = 1) {
+                          const beam::BoundaryArgs* bnd = nullptr, int ksplit = 1,
+                          bool aligned = false) {
   const beam::AlignTables at = align_tables(L, ws);
   float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
   const beam::Shape s = shape_of(c, T);
@@ -253,7 +254,7 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
   const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
 
   if (e_count > 0) {
-    LAUNCH(2, beam::launch_align(ids, tw, at, s, L.bm, e_begin, e_count, st));
+    if (!aligned) LAUNCH(2, beam::launch_align(ids, tw, at, s, L.bm, e_begin, e_count, st));
     if (c.w_dtype == BEAM_F32) {
       float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
       LAUNCH(4, beam::launch_gate_up_f32(reinterpret_cast<const float*>(x),
@@ -411,6 +412,12 @@ beam_status_t forward_impl(const void* x, const float* w_router, const float* bi
   if (beam::use_small_route(s)) {   // partial logits, selection summing them
     float* part = reinterpret_cast<float*>(ws + L.sb);
     LAUNCH(0, beam::launch_router_partials(x, c.x_dtype == BEAM_BF16, w_router, part, s, st));
+    if (beam::use_fused_select_align(s)) {   // the selection and the align in one launch
+      LAUNCH(1, beam::launch_select_align_small(part, bias, ids, tw, align_tables(L, ws), s, L.bm,
+                                                st));
+      return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale,
+                         w_down_scale, out, 0, c.n_experts, false, st, nullptr, 1, true);
+    }
     LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
   } else {
     LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
@@ -670,6 +677,12 @@ beam_status_t beam_moe_forward_boundary(const void* x, const float* w_router, co
   if (beam::use_small_route(s)) {
     float* part = reinterpret_cast<float*>(ws + L.sb);
     LAUNCH(0, beam::launch_router_partials(x, true, w_router, part, s, st));
+    if (beam::use_fused_select_align(s)) {   // as in beam_moe_forward
+      LAUNCH(1, beam::launch_select_align_small(part, bias, ids, tw, align_tables(L, ws), s, L.bm,
+                                                st));
+      return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale,
+                         w_down_scale, nullptr, 0, c.n_experts, false, st, &bnd, 1, true);
+    }
     LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
   } else {
     LAUNCH(0, beam::launch_router_logits(x, true, w_router, bias, sb, s, st));

@@ -86,6 +86,14 @@ hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const 
 hipError_t launch_fill_dense_routes(int32_t* ids, float* w, int64_t n, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, const float* topk_w, const AlignTables& at,
                         const Shape& s, int BM, int e_begin, int e_count, hipStream_t st);
+// T <= kFusedSelectT: the selection from partial logits and the align of its routes, one launch
+// of one workgroup (a wave per token; larger small batches select over many workgroups first)
+constexpr int64_t kFusedSelectT = 16;
+inline bool use_fused_select_align(const Shape& s) {
+  return s.T <= kFusedSelectT && s.K <= 16 && s.T <= kSmallRouteT;
+}
+hipError_t launch_select_align_small(const float* part, const float* bias, int32_t* ids, float* w,
+                                     const AlignTables& at, const Shape& s, int BM, hipStream_t st);
 // bf16 or FP8 experts; FP8 needs the activation scales (per token for x, per sorted row for h)
 // and the per-output-channel weight scales.
 hipError_t launch_gate_up(const void* x, const void* w_gu, uint16_t* hbuf, const float* x_scale,

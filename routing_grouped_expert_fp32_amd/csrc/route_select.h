@@ -14,6 +14,37 @@
 
 namespace beam {
 
+// Wave-wide max / min of a 32-bit unsigned value, returned to every lane: DPP steps inside each row
+// of 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row results read as
+// scalars.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t rows_u32(uint32_t v, int i) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 16 * i);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));    // quad_perm(1,0,3,2)
+  v = max(v, dpp_u32<0x4E>(v));    // quad_perm(2,3,0,1)
+  v = max(v, dpp_u32<0x141>(v));   // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));   // row_mirror
+  return max(max(rows_u32(v, 0), rows_u32(v, 1)), max(rows_u32(v, 2), rows_u32(v, 3)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(v));
+  v = min(v, dpp_u32<0x4E>(v));
+  v = min(v, dpp_u32<0x141>(v));
+  v = min(v, dpp_u32<0x140>(v));
+  return min(min(rows_u32(v, 0), rows_u32(v, 1)), min(rows_u32(v, 2), rows_u32(v, 3)));
+}
+// Order-preserving key of a float that is not NaN: a > b exactly when key(a) > key(b) (-0 is
+// turned into +0 first, so equal values have equal keys).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Score sources. get4(t, lane, s, b) fills, for the lane's experts e = lane + 64 j (j < 4, e < E),
 // s = sigmoid(logit) and b = s + bias[e].
 struct ScoresFromPairs {   // (s, b) pairs written by the logits kernel, [T][E]
@@ -47,16 +78,17 @@ struct ScoresFromPartials {
 #pragma unroll
     for (int j = 0; j < 4; ++j) base[j] = t * E + min(lane + 64 * j, E - 1);
     const int64_t chunk = T * E;
-    for (int q0 = 0; q0 < KS; q0 += 4) {
-      float v[4][4];
+    constexpr int BATCH = 8;
+    for (int q0 = 0; q0 < KS; q0 += BATCH) {
+      float v[BATCH][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < BATCH; ++u) {
         const int64_t off = (int64_t)min(q0 + u, KS - 1) * chunk;
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[u][j] = part[off + base[j]];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < BATCH; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (q0 + u < KS) z[j] = (q0 + u == 0) ? v[u][j] : z[j] + v[u][j];
@@ -134,22 +166,17 @@ __device__ __forceinline__ void select_token(const Src& src, int64_t t, int lane
         v = cv[j];
         e = lane + 64 * j;
       }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(v, off);
-      const int oe = __shfl_xor(e, off);
-      if (ov > v || (ov == v && oe < e)) {
-        v = ov;
-        e = oe;
-      }
-    }
+    // the largest value, then the lowest expert index among the lanes holding it
+    const uint32_t key = order_key(v);
+    const uint32_t kmax = wave_max_u32(key);
+    e = (int)wave_min_u32(key == kmax ? (uint32_t)e : 0xFFFFFFFFu);
     // every lane now holds the winner e; its owner retires it
     const int owner = e & 63, slotj = e >> 6;
-    float s_win = 0.f;
+    float s_mine = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (j == slotj) s_win = sv[j];
-    s_win = __shfl(s_win, owner);
+      if (j == slotj) s_mine = sv[j];
+    const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_mine), owner));
     if (lane == owner) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)

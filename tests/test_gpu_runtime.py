@@ -58,7 +58,7 @@ def test_graph_replay_equals_eager(w_dtype, T):
 
 
 def test_timing_stage_mask():
-    run, _, _ = _case("bf16", 64)
+    run, _, _ = _case("bf16", 16)
     run()
     torch.cuda.synchronize()
     bm.timing_enable(True, stages=["gate_up"])
@@ -71,6 +71,16 @@ def test_timing_stage_mask():
     assert all(n == 0 for k, (_, n) in st.items() if k != "gate_up"), st
     bm.timing_enable(True)
     run()
+    torch.cuda.synchronize()
+    bm.timing_enable(False)
+    st = bm.timing_collect()
+    # up to 16 tokens the selection and the align are one launch (recorded as router_select)
+    for k in ("router_logits", "router_select", "gate_up", "down", "combine"):
+        assert st[k][1] == 1, (k, st)
+    assert st["moe_align"][1] == 0, st
+    run2, _, _ = _case("bf16", 17)
+    bm.timing_enable(True)
+    run2()
     torch.cuda.synchronize()
     bm.timing_enable(False)
     st = bm.timing_collect()
