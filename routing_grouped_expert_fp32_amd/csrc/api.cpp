@@ -278,7 +278,9 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
                                             xs, st));
       LAUNCH(4, beam::launch_gate_up(xq, w_gate_up, hbuf, xs, w_gate_up_scale, true, at, s,
                                      L.max_blocks, small, st));
-      LAUNCH(5, beam::launch_quant_rows_fp8(hbuf, T * c.topk, c.d_ff, hq, hs, st));
+      // a routed call's sorted rows are its local slots only: quantise those (count on the device)
+      LAUNCH(5, beam::launch_quant_rows_fp8(hbuf, T * c.topk, c.d_ff, hq, hs, st,
+                                            filter ? at.expert_off + e_count : nullptr));
       LAUNCH(6, beam::launch_down(hq, w_down, hs, w_down_scale, true, ybuf, at, s,
                                   L.max_blocks, small, st, ksplit));
     }

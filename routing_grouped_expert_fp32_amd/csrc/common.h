@@ -116,8 +116,9 @@ hipError_t launch_gate_up_f32(const float* x, const float* w_gu, float* hbuf,
 hipError_t launch_down_f32(const float* hbuf, const float* w_dn, const float* topk_w, float* ybuf,
                            const AlignTables& at, const Shape& s, int64_t max_blocks,
                            hipStream_t st);
+// n_rows (device, nullable): rows at or past *n_rows are skipped
 hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
-                                 float* scales, hipStream_t st);
+                                 float* scales, hipStream_t st, const int32_t* n_rows = nullptr);
 hipError_t launch_convert(const float* src, int64_t n, bool to_fp8, void* dst, hipStream_t st);
 hipError_t launch_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, const float* C, float* D,
                                 int64_t n, hipStream_t st);

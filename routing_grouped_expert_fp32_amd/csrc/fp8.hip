@@ -30,12 +30,29 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
   return sign | (exp << 3) | man;
 }
 
-// one workgroup per row; cols % 8 == 0 (8 values = one 16-byte load)
+// Four codes packed in a word, by the hardware conversion (round to nearest even, OCP E4M3FN on
+// gfx950). The quantisers feed it fp32(v * 448 / amax), whose magnitude is at most 448 plus a
+// rounding, where it agrees with e4m3_rne_sat (checked against the oracle's codes bit for bit);
+// e4m3_rne_sat stays the encoder of beam_moe_convert, whose inputs can exceed the FP8 range.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+// eight bf16 values (one 16-byte load) -> eight codes
+__device__ __forceinline__ u32x2 encode8(const u32x4& q, float inv) {
+  return u32x2{e4m3x4(bf16_lo(q.x) * inv, bf16_hi(q.x) * inv, bf16_lo(q.y) * inv, bf16_hi(q.y) * inv),
+               e4m3x4(bf16_lo(q.z) * inv, bf16_hi(q.z) * inv, bf16_lo(q.w) * inv, bf16_hi(q.w) * inv)};
+}
+
+// one workgroup per row; cols % 8 == 0 (8 values = one 16-byte load). n_rows (device, nullable):
+// rows at or past *n_rows are not quantised (a routed call's h holds only its local rows).
 __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __restrict__ src,
                                                              int cols, uint8_t* __restrict__ codes,
-                                                             float* __restrict__ scales) {
+                                                             float* __restrict__ scales,
+                                                             const int32_t* __restrict__ n_rows) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
+  if (n_rows && row >= *n_rows) return;   // whole workgroup
   const uint16_t* p = src + row * cols;
   const int n8 = cols >> 3;
   float amax = 0.f;
@@ -56,17 +73,7 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __r
   if (threadIdx.x == 0) scales[row] = zero ? 1.0f : __fdiv_rn(amax, 448.0f);
   for (int c = threadIdx.x; c < n8; c += 256) {
     const u32x4 q = *reinterpret_cast<const u32x4*>(p + 8 * c);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t out[2] = {0u, 0u};
-    if (!zero) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = e4m3_rne_sat(bf16_lo(w[i]) * inv);
-        const uint32_t hi = e4m3_rne_sat(bf16_hi(w[i]) * inv);
-        out[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
-      }
-    }
-    *reinterpret_cast<u32x2*>(codes + row * cols + 8 * c) = u32x2{out[0], out[1]};
+    *reinterpret_cast<u32x2*>(codes + row * cols + 8 * c) = zero ? u32x2{0u, 0u} : encode8(q, inv);
   }
 }
 
@@ -79,10 +86,11 @@ template <int CH>
 __global__ __launch_bounds__(256) void quant_rows_fp8_wave_kernel(const uint16_t* __restrict__ src,
                                                              int64_t rows, int cols,
                                                              uint8_t* __restrict__ codes,
-                                                             float* __restrict__ scales) {
+                                                             float* __restrict__ scales,
+                                                             const int32_t* __restrict__ n_rows) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;   // whole wave; no workgroup barrier below
+  if (row >= rows || (n_rows && row >= *n_rows)) return;   // whole wave; no workgroup barrier below
   const uint16_t* p = src + row * cols;
   const int n8 = cols >> 3;
   auto amax8 = [](const u32x4& q, float m) {
@@ -90,19 +98,6 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_wave_kernel(const uint16_t
 #pragma unroll
     for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
     return m;
-  };
-  auto encode8 = [](const u32x4& q, float inv, bool zero) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t out[2] = {0u, 0u};
-    if (!zero) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = e4m3_rne_sat(bf16_lo(w[i]) * inv);
-        const uint32_t hi = e4m3_rne_sat(bf16_hi(w[i]) * inv);
-        out[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
-      }
-    }
-    return u32x2{out[0], out[1]};
   };
   float amax = 0.f;
   u32x4 q[CH];
@@ -122,7 +117,7 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_wave_kernel(const uint16_t
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = lane + 64 * i;
-    if (c < n8) *reinterpret_cast<u32x2*>(o + 8 * c) = encode8(q[i], inv, zero);
+    if (c < n8) *reinterpret_cast<u32x2*>(o + 8 * c) = zero ? u32x2{0u, 0u} : encode8(q[i], inv);
   }
 }
 
@@ -187,21 +182,21 @@ hipError_t launch_convert(const float* src, int64_t n, bool to_fp8, void* dst, h
 }
 
 hipError_t launch_quant_rows_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes,
-                                 float* scales, hipStream_t st) {
+                                 float* scales, hipStream_t st, const int32_t* n_rows) {
   if (rows == 0) return hipSuccess;
   const int64_t per_lane = ceil_div((int64_t)cols / 8, 64);   // 16-byte pieces per lane of a wave
   if (rows >= 16384 && per_lane <= 8) {
     const dim3 grid((unsigned)ceil_div(rows, 4));
     if (per_lane <= 5)
       hipLaunchKernelGGL(quant_rows_fp8_wave_kernel<5>, grid, dim3(256), 0, st, src, rows, cols,
-                         codes, scales);
+                         codes, scales, n_rows);
     else
       hipLaunchKernelGGL(quant_rows_fp8_wave_kernel<8>, grid, dim3(256), 0, st, src, rows, cols,
-                         codes, scales);
+                         codes, scales, n_rows);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, st, src, cols,
-                     codes, scales);
+                     codes, scales, n_rows);
   return hipGetLastError();
 }
 

@@ -205,14 +205,16 @@ def rel(a, b, rms):
 
 
 def check_batch(out_gpu, x, ids, w_oracle, st, get_expert, contract, n_experts, expert_sel=None,
-                token_sel=None, say=None, y_parts=1):
+                token_sel=None, say=None, y_parts=1, routed=False):
     """Every-row check of one forward. out_gpu [T][H] (torch or numpy), x [T][H] torch (bf16), ids
     [T][K] int64 (the GPU's routes), w_oracle [T][K] float64 (oracle weights for those routes), st from
     read_state, get_expert(e) -> expert_f64 dict. expert_sel / token_sel: if given, only the rows of
     those experts plus every row of those tokens are checked (out only for tokens all of whose slots
-    were checked). Each slot's output and each token's out must lie within the elementwise bound of
-    the down projection of the GPU's own h (FP32 accumulation; for FP8 also the per-block bound of
-    the FP8 instructions); out must meet the block's bar against the pure oracle on every token that
+    were checked). routed: a call over a local expert range; ids hold local expert indices and -1
+    for slots outside the range, and out sums only the local slots (exactly zero for a token with
+    none; tokens_checked counts the others). Each slot's output and each token's out must lie within
+    the elementwise bound of the down projection of the GPU's own h (FP32 accumulation; for FP8 also
+    the per-block bound of the FP8 instructions); out must meet the block's bar against the pure oracle on every token that
     is not a near-flip token. Returns a stats dict; raises AssertionError on a failure."""
     if say is None:
         import parity
@@ -285,8 +287,21 @@ def check_batch(out_gpu, x, ids, w_oracle, st, get_expert, contract, n_experts, 
         err_y = rel(Yg, Yo, rms_y)
         ratio_y = float(np.max(np.abs(Yg - Yo) / (Db + 1e-300)))
         del Yg, Yo, Db, excess
-    # out over the tokens all of whose slots were checked, k order from slot k = 0
-    full = np.nonzero((pos.reshape(T, K) >= 0).all(axis=1))[0]
+    # out over the tokens all of whose slots were checked, k order from slot k = 0 (routed: every
+    # token, over its local slots)
+    if routed:   # a token with no local slot must come out exactly zero
+        has = (ids >= 0).any(axis=1)
+        none = np.nonzero(~has)[0]
+        if len(none):
+            o0 = out_gpu[torch.as_tensor(none)] if isinstance(out_gpu, torch.Tensor) else out_gpu[none]
+            assert not np.asarray(o0.cpu() if isinstance(o0, torch.Tensor) else o0).any(), \
+                "out of a token with no local slot"
+        full = np.nonzero(has)[0]
+        Yh = np.concatenate([Yh, np.zeros((1, H))])
+        DY = np.concatenate([DY, np.zeros((1, H))])
+        pos = np.where(pos >= 0, pos, len(Yh) - 1)
+    else:
+        full = np.nonzero((pos.reshape(T, K) >= 0).all(axis=1))[0]
     og = np.asarray(out_gpu[torch.as_tensor(full)].cpu() if isinstance(out_gpu, torch.Tensor)
                     else out_gpu[full], dtype=np.float64)
     o_h = np.zeros((len(full), H))

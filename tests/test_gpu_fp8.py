@@ -47,6 +47,32 @@ def test_quant_fp8_bitwise_against_oracle():
     assert np.array_equal(c2.cpu().numpy(), w2c) and np.array_equal(s2.cpu().numpy(), w2s)
 
 
+def test_quant_fp8_every_bf16_value():
+    """Every finite bf16 value of magnitude at most 448 (both signs, zeros and subnormals), quantised
+    in rows whose amax is 448 (scale 1): each code is the E4M3 rounding of the value itself, against
+    the oracle bit for bit; and the same values in rows of other amax (general fp32 products)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]                 # finite patterns only
+    vals = codecs.bf16_bits_to_f64(bits)
+    vals = vals[np.abs(vals) <= 448.0]
+    per = 2559
+    n_rows = -(-len(vals) // per)
+    rows = np.zeros((n_rows, 2560))
+    rows[:, 0] = 448.0
+    flat = np.zeros(n_rows * per)
+    flat[:len(vals)] = vals
+    rows[:, 1:] = flat.reshape(n_rows, per)
+    for scale in (1.0, 3.0 / 7.0, 1e-3 * 1.7):
+        x = torch.tensor(rows * scale, dtype=torch.float32).to(torch.bfloat16)
+        codes, scales = bm.quant_fp8(x.cuda())
+        torch.cuda.synchronize()
+        want_c, want_s = codecs.quant_rows_fp8(x.float().numpy())
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), want_s.view(np.uint32)), scale
+        got = codes.cpu().numpy()
+        assert np.array_equal(got, want_c), (scale, np.argwhere(got != want_c)[:5])
+    _say("every bf16 value quantised:", len(vals))
+
+
 @pytest.mark.parametrize("cols", [2560, 4096])
 def test_quant_fp8_many_rows_bitwise_sampled(cols):
     """Prefill-sized row counts (16384 or more rows of up to 4096 values) take the quantiser that

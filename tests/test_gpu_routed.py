@@ -168,3 +168,45 @@ def test_fp8_decode_range():
     err, rms = parity.rel_err(got.cpu().numpy(), ref)
     _say("fp8 decode range max|err|/rms", err)
     assert err <= parity.TOL["fp8"]
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
+def test_tiled_range_every_row(w_dtype):
+    """A routed call over one group of experts (32..63) at T = 300 (tiled kernels; FP8 quantises only
+    the call's own sorted rows) through the every-row check (fullcheck.py): each local row's h, codes
+    and output, and every token's sum over its local slots at the bar except counted near-flip
+    tokens."""
+    import fullcheck
+    name = "fp8_decode" if w_dtype == "fp8" else "decode"
+    wl = synthgen.WORKLOADS[name]
+    W = synthgen.make_inputs(name, device="cuda", T=1)
+    d = synthgen.make_inputs(wl, device="cuda", T=300, with_experts=False)
+    cfg = bm.WorkloadCfg.of(wl.shape, "bf16", w_dtype)
+    T, b, e = 300, 32, 64
+    kw, kw_l = {}, {}
+    if w_dtype == "fp8":
+        kw = dict(w_gate_up_scale=W["w_gate_up_scale"], w_down_scale=W["w_down_scale"])
+        kw_l = dict(w_gate_up_scale=W["w_gate_up_scale"][b:e], w_down_scale=W["w_down_scale"][b:e])
+    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+    bm.forward(d["x"], W["w_router"], d["bias"], W["w_gate_up"], W["w_down"], cfg,
+               topk_ids_out=ids, topk_w_out=w, **kw)
+    ws = torch.empty(bm.workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    out = bm.forward_routed(d["x"], ids, w, W["w_gate_up"][b:e], W["w_down"][b:e], cfg, b, e,
+                            workspace=ws, **kw_l)
+    torch.cuda.synchronize()
+    ids_c = ids.cpu().numpy().astype(np.int64)
+    local = np.where((ids_c >= b) & (ids_c < e), ids_c - b, -1)
+    fp8 = w_dtype == "fp8"
+
+    def get(i):
+        return fullcheck.expert_f64(W["w_gate_up"][b + i], W["w_down"][b + i], wl.shape.d_ff,
+                                    W["w_gate_up_scale"][b + i] if fp8 else None,
+                                    W["w_down_scale"][b + i] if fp8 else None)
+    st = fullcheck.read_state(ws, cfg, T, fp8)
+    stats = fullcheck.check_batch(out, d["x"], local, w.cpu().numpy().astype(np.float64), st, get,
+                                  w_dtype, e - b, say=_say, routed=True)
+    assert stats["rows_checked"] == int((local >= 0).sum())
+    assert stats["tokens_checked"] == int((local >= 0).any(axis=1).sum())
+    assert stats["err_out_pure"] <= parity.TOL[w_dtype], stats
+    assert stats["near_flip_tokens"] <= max(2, T // 50), stats
