@@ -21,7 +21,9 @@
 //   * Tile order is XCD-aware: workgroup L runs on XCD L % 8; the (block, column-tile) space is cut
 //     into 8 contiguous ranges, one per XCD, walked column-tile fastest, so the workgroups sharing
 //     a block's token rows run together on one XCD's L2 (and consecutive blocks of one expert run
-//     on the same XCD).
+//     on the same XCD). An expert with several blocks (skewed batches, the dense layer) has them
+//     walked in groups of four, column-tile major inside a group, so four blocks share each weight
+//     stage in L2 as well.
 // Epilogues: gate/up  h = bf16( silu(bf16(g)) * bf16(u) ), g/u dequantised first for FP8
 //            (acc * token scale * output-channel scale); down  Y[slot] = topk_w[slot] * y (FP32),
 //            y = acc (* row scale * output-channel scale for FP8). The epilogue operands (down: each
@@ -60,6 +62,11 @@ struct PipeCfg {
   static_assert(kLoadsA % WAVES == 0 && kLoadsB % WAVES == 0, "loads split evenly over waves");
   static_assert((kLoadsA + kLoadsB) / WAVES < 64, "vmcnt range");
 };
+
+// blocks of one expert whose tiles are interleaved (tile order, below): with 32 CUs per XCD, 4
+// blocks x 8 column tiles run at once, sharing each weight stage 4 ways and each token-row stage
+// 8 ways in the XCD's L2
+constexpr int kPGroup = 4;
 
 // cache-policy operand of the direct loads: non-temporal for the weight stream (a weight tile is
 // read once per row block of its expert, so it should not push the shared token rows out of L2)
@@ -143,7 +150,23 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // K split (down only): part ksp of ksplit covers stages [ksp * nk, (ksp + 1) * nk) of the row
   // and writes its partial sums to output row slot * ksplit + ksp
   const int ksp = v / tiles, vt = v - ksp * tiles;
-  const int b = vt / n_ctiles, j = vt % n_ctiles;
+  // An expert's blocks form groups of up to kPGroup consecutive blocks; a group's tiles are walked
+  // column-tile major, so the blocks that read one weight column tile run side by side on one
+  // XCD and that tile streams from HBM about once per group instead of once per block. A
+  // one-block group is walked as before (its column tiles in order, sharing the token rows).
+  int b, j;
+  {
+    const int bn = vt / n_ctiles;                        // block in natural (column-fastest) order
+    const int en = at.blk_expert[bn];
+    const int e_rows0 = at.expert_off[en];
+    const int ib = (at.blk_row0[bn] - e_rows0) / C::BM;  // block index within its expert
+    const int nb = (at.expert_off[en + 1] - e_rows0 + C::BM - 1) / C::BM;
+    const int g0 = ib - ib % kPGroup;
+    const int sz = min(kPGroup, nb - g0);
+    const int off = vt - (bn - (ib - g0)) * n_ctiles;   // tile within the group
+    j = off / sz;
+    b = bn - (ib - g0) + off % sz;
+  }
   const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
 
   // waves: WAVES / 2 wave rows x 2 wave columns; wave row wm takes the 16-row sub-tiles
