@@ -101,7 +101,11 @@ typedef struct beam_moe_cfg {
  *   topk_ids  [T][K] int32 out — chosen experts, biased score descending, ties to the lower id
  *   topk_w    [T][K] fp32 out — routed_scale * s_k / sum_j s_j, s = sigmoid(logit) (unbiased)
  *   workspace device scratch of at least beam_moe_route_workspace_bytes(cfg, T) bytes
- * Ties between equal FP32 scores (groups or experts) go to the lower index. */
+ * Ties between equal FP32 scores (groups or experts) go to the lower index.
+ * Logits are FP32 sums of exact products. With bf16 x and T > 64 each FP32 router weight is split
+ * exactly into three bf16 terms (valid for |w| >= 2^-102; smaller weights lose only bits below
+ * 2^-126), written to the workspace, and the bf16 matrix cores accumulate the products in FP32;
+ * otherwise the FP32 matrix cores multiply x (widened to FP32 if bf16) by the weights directly. */
 BEAM_API beam_status_t beam_moe_route(const void* x, const float* w_router, const float* bias,
                              int32_t* topk_ids, float* topk_w, int64_t T,
                              const beam_moe_cfg* cfg, void* workspace, size_t workspace_bytes,
@@ -132,8 +136,8 @@ BEAM_API size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int64_t T);
 /* beam_moe_forward without a caller workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
  * workspace is a 64 MiB array of device memory the library holds per GPU until the process ends
- * (enough for beam_moe_workspace_bytes(cfg, T) <= 64 MiB: Beam's shape up to 324 tokens with bf16
- * experts, 288 with FP8 ones). The call
+ * (enough for beam_moe_workspace_bytes(cfg, T) <= 64 MiB: Beam's shape up to 327 tokens with bf16
+ * experts, 290 with FP8 ones). The call
  * itself allocates nothing and leaves no state that a later call depends on.
  *   Arguments and results as for beam_moe_forward, without workspace / workspace_bytes.
  *   BEAM_ERR_WORKSPACE: beam_moe_workspace_bytes(cfg, T) exceeds 64 MiB (nothing is launched).
@@ -317,7 +321,8 @@ BEAM_API int32_t beam_moe_version(void);
  * returns the number of stages defined. Stage order: 0 router logits, 1 router select,
  * 2 moe_align, 3 activation quant (fp8), 4 gate/up GEMM, 5 h quant (fp8), 6 down GEMM,
  * 7 combine (for forwards of up to 16 tokens the selection and the align are one launch, recorded
- * as stage 1). beam_moe_stage_name(i) names stage i.
+ * as stage 1; past 64 tokens with bf16 activations the logits and the selection are one launch,
+ * recorded as stage 0 together with the split of the router weights that precedes it). beam_moe_stage_name(i) names stage i.
  * beam_moe_timing_stages(mask) restricts the recording to the stages whose bit (1 << stage) is set
  * (default: all), so a caller can time one kernel without event records between the others. */
 BEAM_API void beam_moe_timing_enable(int32_t enable);

@@ -48,7 +48,7 @@ int block_rows(const beam_moe_cfg& c, int64_t T) {
 struct Layout {
   size_t sb = 0, ids = 0, w = 0, chunk_mask = 0, chunk_base = 0, expert_count = 0, expert_off = 0,
          n_blocks = 0, blk_expert = 0, blk_row0 = 0, blk_rows = 0, sorted = 0, sorted_w = 0, hbuf = 0,
-         ybuf = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
+         ybuf = 0, xq = 0, xs = 0, hq = 0, hs = 0, wsplit = 0, total = 0;
   int64_t max_blocks = 0;
   int bm = 0;
 };
@@ -63,11 +63,20 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full, int ybuf_parts =
     return o;
   };
   const int64_t E = c.n_experts, K = c.topk, TK = T * K;
-  // (s, b) pairs per token and expert, or for small batches the partial logits [H/256][T][E]
-  const int64_t sb_floats = T <= beam::kSmallRouteT
-                                ? std::max<int64_t>(2, c.hidden / 256) * T * E
-                                : 2 * T * E;
-  L.sb = take(sizeof(float) * (size_t)sb_floats);
+  // small batches: the partial logits [H/256][T][E]; larger ones with bf16 activations: the router
+  // weights split into three bf16 planes, 3 E H values (in a forward they share the region of the
+  // expert outputs, which are written only after the routing); otherwise (s, b) pairs [T][E]
+  const bool split_route = c.x_dtype == BEAM_BF16 && T > beam::kSmallRouteT;
+  const size_t split_bytes = split_route ? 6 * (size_t)E * (size_t)c.hidden : 0;
+  size_t sb_bytes;
+  if (T <= beam::kSmallRouteT)
+    sb_bytes = sizeof(float) * (size_t)(std::max<int64_t>(2, c.hidden / 256) * T * E);
+  else if (split_route)
+    sb_bytes = full ? 16 : split_bytes;
+  else
+    sb_bytes = sizeof(float) * (size_t)(2 * T * E);
+  L.sb = take(sb_bytes);
+  L.wsplit = L.sb;
   if (full) {
     const int64_t n_chunks = ceil_div(T, beam::kAlignChunk);
     L.bm = block_rows(c, T);
@@ -93,7 +102,9 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full, int ybuf_parts =
       L.hs = take(sizeof(float) * (size_t)TK);
     }
     // last, so the offsets above do not depend on the number of partial rows per slot
-    L.ybuf = take(sizeof(float) * (size_t)TK * (size_t)ybuf_parts * (size_t)c.hidden);
+    L.ybuf = take(std::max(sizeof(float) * (size_t)TK * (size_t)ybuf_parts * (size_t)c.hidden,
+                           split_bytes));
+    if (split_route) L.wsplit = L.ybuf;
   }
   L.total = off;
   return L;
@@ -297,6 +308,21 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
   return BEAM_OK;
 }
 
+// Routing of a batch past the small-batch path: bf16 activations take the one-pass router
+// (logits and selection in one launch), FP32 ones the logits kernel and then the selection.
+beam_status_t route_large(const void* x, bool x_bf16, const float* w_router, const float* bias,
+                          float2* sb, uint16_t* wsplit, int32_t* ids, float* tw,
+                          const beam::Shape& s, hipStream_t st) {
+  if (beam::use_fused_router(s, x_bf16)) {
+    LAUNCH(0, beam::launch_router_split(w_router, wsplit, s, st));
+    LAUNCH(0, beam::launch_router_fused(x, wsplit, bias, ids, tw, s, st));
+    return BEAM_OK;
+  }
+  LAUNCH(0, beam::launch_router_logits(x, x_bf16, w_router, bias, sb, s, st));
+  LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  return BEAM_OK;
+}
+
 // Boundary arguments: validation common to both boundary entry points.
 beam_status_t make_boundary(const void* h, const float* gamma_post, const float* gamma_next,
                             void* h_out, void* x_next, int32_t hidden, int32_t depth_n, float eps,
@@ -421,9 +447,10 @@ beam_status_t forward_impl(const void* x, const float* w_router, const float* bi
                          w_down_scale, out, 0, c.n_experts, false, st, nullptr, 1, true);
     }
     LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
-  } else {
-    LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
-    LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  } else if ((rc = route_large(x, c.x_dtype == BEAM_BF16, w_router, bias, sb,
+                               reinterpret_cast<uint16_t*>(ws + L.wsplit), ids, tw, s, st)) !=
+             BEAM_OK) {
+    return rc;
   }
   return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
                      out, 0, c.n_experts, false, st);
@@ -562,9 +589,8 @@ beam_status_t beam_moe_route(const void* x, const float* w_router, const float* 
     LAUNCH(1, beam::launch_router_select_partials(part, bias, topk_ids, topk_w, s, st));
     return BEAM_OK;
   }
-  LAUNCH(0, beam::launch_router_logits(x, c.x_dtype == BEAM_BF16, w_router, bias, sb, s, st));
-  LAUNCH(1, beam::launch_router_select(sb, topk_ids, topk_w, s, st));
-  return BEAM_OK;
+  return route_large(x, c.x_dtype == BEAM_BF16, w_router, bias, sb,
+                     reinterpret_cast<uint16_t*>(ws + L.wsplit), topk_ids, topk_w, s, st);
 }
 
 beam_status_t beam_moe_forward(const void* x, const float* w_router, const float* bias,
@@ -686,9 +712,10 @@ beam_status_t beam_moe_forward_boundary(const void* x, const float* w_router, co
                          w_down_scale, nullptr, 0, c.n_experts, false, st, &bnd, 1, true);
     }
     LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
-  } else {
-    LAUNCH(0, beam::launch_router_logits(x, true, w_router, bias, sb, s, st));
-    LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
+  } else if ((rc = route_large(x, true, w_router, bias, sb,
+                               reinterpret_cast<uint16_t*>(ws + L.wsplit), ids, tw, s, st)) !=
+             BEAM_OK) {
+    return rc;
   }
   return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
                      nullptr, 0, c.n_experts, false, st, &bnd);

@@ -83,6 +83,14 @@ hipError_t launch_router_select_partials(const float* part, const float* bias, i
                                          float* w, const Shape& s, hipStream_t st);
 hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const Shape& s,
                                 hipStream_t st);
+// bf16 activations and T > kSmallRouteT: the router weights split exactly into three bf16 planes
+// (3 E H bf16, in MFMA fragment order; launch_router_split), then logits and selection in one
+// launch with no HBM round trip
+bool use_fused_router(const Shape& s, bool x_bf16);
+hipError_t launch_router_split(const float* w_router, uint16_t* planes, const Shape& s,
+                               hipStream_t st);
+hipError_t launch_router_fused(const void* x, const uint16_t* planes, const float* bias,
+                               int32_t* ids, float* w, const Shape& s, hipStream_t st);
 hipError_t launch_fill_dense_routes(int32_t* ids, float* w, int64_t n, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, const float* topk_w, const AlignTables& at,
                         const Shape& s, int BM, int e_begin, int e_count, hipStream_t st);

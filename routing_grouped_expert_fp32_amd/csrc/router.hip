@@ -162,6 +162,245 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const void* __restr
 }
 
 // ---------------------------------------------------------------------------------------------
+// One-pass router for bf16 activations (T > kSmallRouteT): logits, sigmoid, bias and selection in
+// one workgroup per 32 tokens; the logits never leave the chip.
+//
+// Exact split of the FP32 weights, once per call (router_split_kernel): w = hi + mid + lo with three
+// bf16 values (hi: w truncated to its leading 8 significant bits; mid: the leading 8 bits of the
+// exact remainder w - hi; lo: the rest, at most 8 bits, so exact), valid for |w| >= 2^-102 (the
+// remainders stay normal; smaller weights lose only bits below 2^-126, far below any logit's FP32
+// rounding). A bf16 activation times each part is exact in FP32, so x.w = x.hi + x.mid + x.lo with
+// no rounding before the FP32 accumulation of the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, 16x
+// the FP32 MFMA rate: three products cost about a fifth of one FP32 MFMA pass). hi products go to
+// one FP32 accumulator, mid and lo products to a second; z = acc_hi + acc_lo.
+// The planes are stored in MFMA fragment order, so each wave load of the one-pass router reads
+// 1 KB contiguous: fragment (expert tile nt, 32-deep step s, plane p) is 64 lanes x 8 bf16 at
+// ((nt * H/32 + s) * 3 + p) * 512 elements, lane 16 g + r holding expert 16 nt + r, hidden
+// 32 s + 8 g .. + 7.
+constexpr int kSplitPerThread = 8;
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
+                                                           uint16_t* __restrict__ planes,
+                                                           int64_t n, int H) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kSplitPerThread;
+  if (i >= n) return;   // n % 8 == 0 (H % 256 == 0)
+  const int e = (int)(i / H), k0 = (int)(i % H);
+  const int64_t frag = ((int64_t)(e >> 4) * (H / 32) + (k0 >> 5)) * 3;
+  const int lane = 16 * ((k0 & 31) >> 3) + (e & 15);
+  uint16_t* const dst = planes + frag * 512 + 8 * lane;
+  const floatx4 a = *reinterpret_cast<const floatx4*>(wr + i);
+  const floatx4 b = *reinterpret_cast<const floatx4*>(wr + i + 4);
+  const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  u32x4 h, m, l;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float v = w[2 * p + q];
+      hb[q] = __float_as_uint(v) & 0xFFFF0000u;
+      const float r1 = v - __uint_as_float(hb[q]);              // exact
+      mb[q] = __float_as_uint(r1) & 0xFFFF0000u;
+      lb[q] = __float_as_uint(r1 - __uint_as_float(mb[q]));     // exact, <= 8 significant bits
+    }
+    h[p] = (hb[0] >> 16) | hb[1];   // element 2p in the low half
+    m[p] = (mb[0] >> 16) | mb[1];
+    l[p] = (lb[0] >> 16) | (lb[1] & 0xFFFF0000u);
+  }
+  *reinterpret_cast<u32x4*>(dst) = h;
+  *reinterpret_cast<u32x4*>(dst + 512) = m;
+  *reinterpret_cast<u32x4*>(dst + 1024) = l;
+}
+
+// Scores of one token from its logits row in LDS.
+struct ScoresFromLogits {
+  const float* z;      // [E] logits of the token
+  const float* bias;
+  int E;
+  __device__ void get4(int64_t, int lane, float* s, float* b) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) {
+        s[j] = 1.0f / (1.0f + expf(-z[e]));
+        b[j] = s[j] + bias[e];
+      }
+    }
+  }
+};
+
+// WG = 8 waves, 32 tokens x all E experts (E <= 256, E % 16 == 0). Wave w owns the expert tiles
+// w and w + 8 (16 experts each) for both 16-token tiles, over the whole hidden dimension, in 32-deep
+// MFMA steps. Token rows go through an LDS ring of 256-wide hidden chunks (rows padded to 528 B so
+// the 16 rows of a fragment read fall on distinct banks), loaded into registers one chunk ahead
+// and stored after the chunk's MFMAs; each wave's weight fragments (three planes) stream from L2
+// straight into registers, kPrefW steps ahead. Then the logits go to LDS and each wave selects 4
+// tokens (select_token).
+constexpr int kRfTM = 32, kRfWaves = 8, kRfChunk = 256, kRfRowBytes = 2 * kRfChunk + 16;
+constexpr int kRfSteps = kRfChunk / 32;   // MFMA steps per chunk
+constexpr int kPrefW = 4;                 // weight steps in flight
+__global__ __launch_bounds__(64 * kRfWaves, 1) void router_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wout, int64_t T,
+    int H, int E, int G, int Gk, int K, float scale) {
+  constexpr int MB = kRfTM / 16, NB = 2;
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][kRfTM * kRfRowBytes];
+  __shared__ float zl[kRfTM][256 + 1];
+  __shared__ float bl[kRfWaves][256];
+  __shared__ float gsc[kRfWaves][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kRfTM;
+  const int n_et = E / 16;
+
+  // token-row chunk loads: thread -> row tid / 16, 16-byte pieces tid % 16 and tid % 16 + 16
+  const int xr = tid >> 4, xc = tid & 15;
+  const int64_t xrow = min(t0 + xr, T - 1);   // tail rows re-read a valid row
+  const uint16_t* xsrc = x + xrow * H + 8 * xc;
+  u32x4 xv[2];
+  auto load_x = [&](int chunk) {
+    const uint16_t* p = xsrc + chunk * kRfChunk;
+    xv[0] = *reinterpret_cast<const u32x4*>(p);
+    xv[1] = *reinterpret_cast<const u32x4*>(p + 128);
+  };
+  auto store_x = [&](int slot) {
+    unsigned char* d = xs[slot] + xr * kRfRowBytes + 16 * xc;
+    *reinterpret_cast<u32x4*>(d) = xv[0];
+    *reinterpret_cast<u32x4*>(d + 256) = xv[1];
+  };
+
+  // weight fragments of expert tile nt = wave + 8 i, in fragment order (router_split_kernel): lane
+  // 16 g + r gets expert 16 nt + r, hidden 8 g .. 8 g + 7 of each step and plane (tiles past E
+  // read tile 0 and are discarded)
+  const int nsteps = H / 32;
+  const uint16_t* wsrc[NB];
+  bool wvalid[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int nt = wave + kRfWaves * i;
+    wvalid[i] = nt < n_et;
+    wsrc[i] = planes + (int64_t)(wvalid[i] ? nt : 0) * nsteps * 3 * 512 + 8 * lane;
+  }
+  bf16x8 wb[kPrefW][NB][3];
+  auto load_w = [&](int buf, int step) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        wb[buf][i][p] = *reinterpret_cast<const bf16x8*>(wsrc[i] + (3 * step + p) * 512);
+  };
+
+  floatx4 acc_h[MB][NB], acc_l[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      acc_h[m][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc_l[m][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  load_x(0);
+  store_x(0);
+  // the prologue issues the ring in the steady-state order (oldest first), so the first wait of
+  // the loop is as partial as the others
+#pragma unroll
+  for (int u = 0; u < kPrefW; ++u) {
+    load_w(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nchunks = H / kRfChunk;
+  static_assert(kRfSteps % kPrefW == 0, "weight ring turns over within a chunk");
+  // Loads and MFMAs are unconditional inside the loop (past the end they re-read the last chunk /
+  // step, and tiles past E compute on tile 0's rows and are discarded), so the loop has no branches
+  // and the weight ring stays in fixed registers with partial vmcnt waits.
+  for (int c = 0; c < nchunks; ++c) {
+    __syncthreads();   // chunk c is in LDS; everyone is done with chunk c - 1's slot
+    load_x(min(c + 1, nchunks - 1));
+    const unsigned char* sa = xs[c & 1];
+#pragma unroll
+    for (int s0 = 0; s0 < kRfSteps; s0 += kPrefW) {
+#pragma unroll
+      for (int u = 0; u < kPrefW; ++u) {
+        const int step = c * kRfSteps + s0 + u;
+        bf16x8 af[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          af[m] = *reinterpret_cast<const bf16x8*>(sa + (16 * m + r) * kRfRowBytes +
+                                                   64 * (s0 + u) + 16 * g);
+        bf16x8 bw[NB][3];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int p = 0; p < 3; ++p) bw[i][p] = wb[u][i][p];
+        load_w(u, min(step + kPrefW, nsteps - 1));
+        // keep the prefetch here: without this fence the scheduler sinks each load next to its
+        // use four steps later and waits for it there
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            acc_h[m][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bw[i][0], acc_h[m][i], 0,
+                                                                  0, 0);
+            acc_l[m][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bw[i][1], acc_l[m][i], 0,
+                                                                  0, 0);
+            acc_l[m][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bw[i][2], acc_l[m][i], 0,
+                                                                  0, 0);
+          }
+      }
+    }
+    store_x((c + 1) & 1);   // (the last chunk stores into the idle slot)
+  }
+  // logits to LDS: lane holds tokens 4 g + q, expert 16 nt + r of each tile
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if (!wvalid[i]) continue;
+    const int e = 16 * (wave + kRfWaves * i) + r;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zl[16 * m + 4 * g + q][e] = acc_h[m][i][q] + acc_l[m][i][q];
+  }
+  __syncthreads();
+  for (int tl = wave; tl < kRfTM; tl += kRfWaves) {
+    const int64_t t = t0 + tl;
+    if (t >= T) break;   // wave-uniform
+    int id;
+    float w;
+    select_token(ScoresFromLogits{zl[tl], bias, E}, t, lane, bl[wave], gsc[wave], E, G, Gk, K,
+                 scale, id, w);
+    if (lane < K) {
+      ids[t * K + lane] = id;
+      wout[t * K + lane] = w;
+    }
+  }
+}
+
+bool use_fused_router(const Shape& s, bool x_bf16) {
+  return x_bf16 && s.T > kSmallRouteT && s.E <= 256 && s.E % 16 == 0 && s.H % kRfChunk == 0 &&
+         s.G <= 64 && s.K <= 64;
+}
+
+hipError_t launch_router_split(const float* w_router, uint16_t* planes, const Shape& s,
+                               hipStream_t st) {
+  const int64_t n = (int64_t)s.E * s.H;
+  if (n % kSplitPerThread) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)ceil_div(n / kSplitPerThread, 256)),
+                     dim3(256), 0, st, w_router, planes, n, s.H);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_fused(const void* x, const uint16_t* planes, const float* bias,
+                               int32_t* ids, float* w, const Shape& s, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (!use_fused_router(s, true)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(router_fused_kernel, dim3((unsigned)ceil_div(s.T, kRfTM)),
+                     dim3(64 * kRfWaves), 0, st, reinterpret_cast<const uint16_t*>(x), planes,
+                     bias, ids, w, s.T, s.H, s.E, s.G, s.Gk, s.K, s.scale);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 // Selection: one wave per token, 4 tokens per WG (select_token in route_select.h).
 template <class Src>
 __global__ __launch_bounds__(256) void router_select_kernel(Src src, int32_t* __restrict__ ids,

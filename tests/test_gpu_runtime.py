@@ -86,6 +86,18 @@ def test_timing_stage_mask():
     st = bm.timing_collect()
     for k in ("router_logits", "router_select", "moe_align", "gate_up", "down", "combine"):
         assert st[k][1] == 1, (k, st)
+    # past 64 tokens bf16 activations take the one-pass router, after the split of the router
+    # weights (both recorded as router_logits)
+    run3, _, _ = _case("bf16", 100)
+    bm.timing_enable(True)
+    run3()
+    torch.cuda.synchronize()
+    bm.timing_enable(False)
+    st = bm.timing_collect()
+    assert st["router_logits"][1] == 2, st
+    for k in ("moe_align", "gate_up", "down", "combine"):
+        assert st[k][1] == 1, (k, st)
+    assert st["router_select"][1] == 0, st
 
 
 def test_two_streams_with_their_own_workspaces():
