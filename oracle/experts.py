@@ -120,23 +120,6 @@ def forward_routed(x, ids, w, get_expert: Callable[[int], dict], contract: str,
     return out
 
 
-def forward_token_major(x, ids, w, get_expert: Callable[[int], dict], contract: str):
-    """Same result as forward_expert_major, computed one token and one expert at a time."""
-    x = to_f64(x)
-    T, K = np.asarray(ids).shape
-    out = None
-    for t in range(T):
-        acc = None
-        for k in range(K):
-            y = expert_mlp(x[t:t + 1], get_expert(int(ids[t][k])), contract)[0]
-            c = float(w[t][k]) * y
-            acc = c if acc is None else acc + c
-        if out is None:
-            out = np.zeros((T, acc.shape[0]), dtype=np.float64)
-        out[t] = acc
-    return out
-
-
 def split_expert(w_gate_up_e, w_down_e, d_ff: int, gate_up_scale=None, down_scale=None) -> dict:
     """Float64 expert dict from one expert's stored tensors (torch or numpy; fp32, bf16 or E4M3
     codes as uint8 when scales are given)."""

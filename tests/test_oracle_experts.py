@@ -122,17 +122,6 @@ def test_identical_experts_closed_form(contract):
     assert np.allclose(out, 2.5 * mlp, rtol=1e-12, atol=1e-13)
 
 
-def test_token_major_equals_expert_major_bitwise():
-    d = synthgen.make_inputs("tiny")
-    sh = d["workload"].shape
-    r = router.route_cfg(d)
-    get = lambda e: experts.split_expert(d["w_gate_up"][e], d["w_down"][e], sh.d_ff)  # noqa: E731
-    for contract in ("fp32", "bf16"):
-        a = experts.forward_expert_major(d["x"][:16], r.ids[:16], r.weights[:16], get, contract)
-        b = experts.forward_token_major(d["x"][:16], r.ids[:16], r.weights[:16], get, contract)
-        assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
-
-
 def test_token_permutation_equivariance():
     d = synthgen.make_inputs("tiny")
     sh = d["workload"].shape
