@@ -23,13 +23,18 @@
  *     base address 16-byte aligned. Inputs are never written. Outputs and the workspace are fully
  *     overwritten (plain stores, never accumulation).
  *   - `stream` is a hipStream_t (NULL = the null stream). Every call is asynchronous on it; none
- *     allocates device memory, frees, or synchronises the host.
+ *     allocates device memory, frees, or synchronises the host (except under BEAM_MOE_SYNC_CHECK).
  *   - Every argument is validated on the host before the first launch: a non-zero status means
  *     nothing was launched. T = 0 is a successful no-op. Device-side faults surface at the caller's
  *     next synchronisation. Unsupported shapes or dtypes return BEAM_ERR_UNSUPPORTED: there is no
  *     fallback path.
  *   - Calls on distinct workspaces may run concurrently on different streams; calls that share a
  *     workspace must be ordered by the caller.
+ *   - Debugging: with the environment variable BEAM_MOE_SYNC_CHECK set to anything but "0" (read
+ *     at the first launch) every launch is followed by a synchronisation of its stream, and a kernel
+ *     that failed is reported on stderr, naming its stage, and returned as BEAM_ERR_LAUNCH by the
+ *     call that launched it. This serialises the host with the GPU; not for use under stream
+ *     capture.
  *   - NaN or infinite inputs give undefined (but memory-safe) results.
  */
 #ifndef BEAM_MOE_H

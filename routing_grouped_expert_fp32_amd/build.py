@@ -14,8 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbeam_moe.so")
-SOURCES = ["api.cpp", "router.hip", "align.hip", "gemm_grouped.hip", "gemm_f32.hip", "fp8.hip",
-           "combine.hip", "boundary.hip"]
+SOURCES = ["api.cpp", "host_rules.cpp", "scratch.hip", "router.hip", "align.hip",
+           "gemm_grouped.hip", "gemm_f32.hip", "fp8.hip", "combine.hip", "boundary.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

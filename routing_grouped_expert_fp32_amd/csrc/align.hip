@@ -19,7 +19,7 @@
 // indices in the tables are local (id - e_begin), so the GEMMs index a local weight array.
 // Slots of one token name distinct experts (the router guarantees it; for given routes a repeated
 // id within a token leaves one of its slots out, which is memory-safe).
-#include "common.h"
+#include "device_common.h"
 #include "route_select.h"
 
 namespace beam {

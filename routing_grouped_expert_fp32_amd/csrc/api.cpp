@@ -1,8 +1,10 @@
 // C ABI of the Beam MoE library: argument validation, workspace carving, kernel dispatch.
 // Declarations, argument meanings and error behaviour: include/beam_moe.h.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <algorithm>
@@ -222,10 +224,29 @@ struct StageTimer {
   }
 };
 
-#define LAUNCH(stage, expr)                               \
-  do {                                                    \
-    StageTimer timer_((stage), st);                       \
-    if ((expr) != hipSuccess) return BEAM_ERR_LAUNCH;     \
+// BEAM_MOE_SYNC_CHECK set to anything but "0" (read once): every launch is followed by a
+// synchronisation of its stream, and a kernel that failed is reported (stderr, naming the stage)
+// as BEAM_ERR_LAUNCH from the call that launched it. A debugging aid: it serialises the host with
+// the GPU and must not be used under stream capture.
+bool sync_check() {
+  static const bool on = [] {
+    const char* v = std::getenv("BEAM_MOE_SYNC_CHECK");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+beam_status_t launched(hipError_t err, hipStream_t st, const char* what) {
+  if (err == hipSuccess && sync_check()) err = hipStreamSynchronize(st);
+  if (err == hipSuccess) return BEAM_OK;
+  std::fprintf(stderr, "beam_moe: %s failed: %s\n", what, hipGetErrorString(err));
+  return BEAM_ERR_LAUNCH;
+}
+
+#define LAUNCH(stage, expr)                                                            \
+  do {                                                                                 \
+    StageTimer timer_((stage), st);                                                    \
+    if (launched((expr), st, kStageNames[(stage)]) != BEAM_OK) return BEAM_ERR_LAUNCH; \
   } while (0)
 
 beam::Shape shape_of(const beam_moe_cfg& c, int64_t T) {
@@ -456,28 +477,6 @@ beam_status_t forward_impl(const void* x, const float* w_router, const float* bi
                      out, 0, c.n_experts, false, st);
 }
 
-// Workspace of the no-allocation entry point: one array per GPU, in device memory the library holds
-// until the process ends. In host code `scratch` names a host-side stand-in, not the device array:
-// the device address comes from hipGetSymbolAddress, once per device with that device current,
-// and only that address is handed to kernels.
-constexpr size_t kScratchBytes = size_t(64) << 20;
-static __device__ __align__(256) unsigned char scratch[kScratchBytes];
-
-beam_status_t scratch_of_current_device(void** out) {
-  static void* ptrs[kMaxDevices];
-  static std::mutex mu;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BEAM_ERR_DEVICE;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!ptrs[dev]) {
-    void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_ERR_DEVICE;
-    ptrs[dev] = p;
-  }
-  *out = ptrs[dev];
-  return BEAM_OK;
-}
-
 // Offset and size of one inspectable array of a forward's workspace (beam_moe_workspace_region).
 beam_status_t region_of(const beam_moe_cfg& c, const Layout& L, int64_t T, int y_parts,
                         int32_t region, size_t* offset, size_t* bytes) {
@@ -612,12 +611,13 @@ beam_status_t beam_moe_forward_noalloc(const void* x, const float* w_router, con
   if (rc != BEAM_OK) return rc;
   if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
   if (T == 0) return BEAM_OK;
-  if (make_layout(*cfg, T, true).total > kScratchBytes) return BEAM_ERR_WORKSPACE;
+  if (make_layout(*cfg, T, true).total > beam::kScratchBytes) return BEAM_ERR_WORKSPACE;
   if ((rc = check_device()) != BEAM_OK) return rc;
   void* scratch_ptr = nullptr;
-  if ((rc = scratch_of_current_device(&scratch_ptr)) != BEAM_OK) return rc;
+  if (beam::scratch_of_current_device(&scratch_ptr) != hipSuccess) return BEAM_ERR_DEVICE;
   return forward_impl(x, w_router, bias, w_gate_up, w_down, out, T, cfg, w_gate_up_scale,
-                      w_down_scale, topk_ids_out, topk_w_out, scratch_ptr, kScratchBytes, stream);
+                      w_down_scale, topk_ids_out, topk_w_out, scratch_ptr, beam::kScratchBytes,
+                      stream);
 }
 
 beam_status_t beam_residual_boundary(const void* y, int32_t y_dtype, const void* h,
@@ -816,7 +816,8 @@ beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_up, const
   char* ws = reinterpret_cast<char*>(workspace);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
   float* tw = reinterpret_cast<float*>(ws + L.w);
-  if (beam::launch_fill_dense_routes(ids, tw, T, st) != hipSuccess) return BEAM_ERR_LAUNCH;
+  if (launched(beam::launch_fill_dense_routes(ids, tw, T, st), st, "dense routes") != BEAM_OK)
+    return BEAM_ERR_LAUNCH;
   // one expert: the tiled down GEMM has ceil(T / BM) x (hidden / 256) workgroups, few enough at
   // prefill sizes that a K split evens out the last round
   int ks = 1;
@@ -842,10 +843,9 @@ beam_status_t beam_moe_quant_fp8(const void* src, int64_t rows, int32_t cols, ui
   beam_status_t rc = check_device();
   if (rc != BEAM_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (beam::launch_quant_rows_fp8(reinterpret_cast<const uint16_t*>(src), rows, cols, codes, scales,
-                                  st) != hipSuccess)
-    return BEAM_ERR_LAUNCH;
-  return BEAM_OK;
+  return launched(beam::launch_quant_rows_fp8(reinterpret_cast<const uint16_t*>(src), rows, cols,
+                                              codes, scales, st),
+                  st, "quant_fp8");
 }
 
 beam_status_t beam_moe_convert(const float* src, int64_t n, int32_t dst_dtype, void* dst,
@@ -859,10 +859,9 @@ beam_status_t beam_moe_convert(const float* src, int64_t n, int32_t dst_dtype, v
   if (any_alias({rng(src, 4 * nb)}, {rng(dst, nb * dtype_bytes(dst_dtype))})) return BEAM_ERR_ALIAS;
   beam_status_t rc = check_device();
   if (rc != BEAM_OK) return rc;
-  if (beam::launch_convert(src, n, dst_dtype == BEAM_FP8_E4M3, dst,
-                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return BEAM_ERR_LAUNCH;
-  return BEAM_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return launched(beam::launch_convert(src, n, dst_dtype == BEAM_FP8_E4M3, dst, st), st,
+                  "convert");
 }
 
 beam_status_t beam_moe_fp8_dot_tiles(const uint8_t* a, const uint8_t* b, const float* c, float* d,
@@ -877,10 +876,8 @@ beam_status_t beam_moe_fp8_dot_tiles(const uint8_t* a, const uint8_t* b, const f
     return BEAM_ERR_ALIAS;
   beam_status_t rc = check_device();
   if (rc != BEAM_OK) return rc;
-  if (beam::launch_fp8_dot_tiles(a, b, c, d, n_tiles, reinterpret_cast<hipStream_t>(stream)) !=
-      hipSuccess)
-    return BEAM_ERR_LAUNCH;
-  return BEAM_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return launched(beam::launch_fp8_dot_tiles(a, b, c, d, n_tiles, st), st, "fp8_dot_tiles");
 }
 
 void beam_moe_timing_enable(int32_t enable) { g_timing = enable != 0; }

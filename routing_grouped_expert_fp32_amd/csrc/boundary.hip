@@ -19,7 +19,7 @@
 // then the four wave sums in wave order (deterministic).
 #include <type_traits>
 
-#include "common.h"
+#include "device_common.h"
 
 namespace beam {
 
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kBndThreads) void boundary_kernel(
   }
 }
 
-int boundary_max_hidden() { return kBndMaxChunks * 4 * kBndThreads; }
+static_assert(kBndMaxChunks * 4 * kBndThreads == kBoundaryMaxHidden, "boundary row width");
 
 hipError_t launch_boundary(const BoundaryArgs& b, const float* Y, int K, const int32_t* ids,
                            int e_begin, int e_end, const void* y, bool y_bf16, int64_t T, int H,

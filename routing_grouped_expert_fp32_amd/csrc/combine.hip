@@ -7,7 +7,7 @@
 // With given routes over a range of experts ([S] §Fusion Optimizations: expert IDs and weights in,
 // complete outputs back, every expert-parallel rank running its own experts) the sum covers the
 // slots routed to the range.
-#include "common.h"
+#include "device_common.h"
 
 namespace beam {
 

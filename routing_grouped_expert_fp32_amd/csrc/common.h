@@ -1,40 +1,17 @@
-// Internal device/host helpers of the Beam MoE library (gfx950 only).
+// Internal declarations of the Beam MoE library shared by the host dispatcher and the kernels
+// (gfx950 only): shapes, workspace tables, sizes and the kernel launchers. Plain C++ plus the HIP
+// runtime API; device-side helpers are in device_common.h.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace beam {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef int intx8 __attribute__((ext_vector_type(8)));
-typedef int intx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kWave = 64;
 constexpr int kAlignChunk = 256;              // tokens per align chunk (one mask bit each)
 constexpr int kAlignWords = kAlignChunk / 64; // 64-bit mask words per (chunk, expert)
-
-// ---- bf16 -------------------------------------------------------------------------------------
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-__device__ __forceinline__ float bf16_round(float f) {
-  return __uint_as_float(f32_to_bf16_bits(f) << 16);
-}
-__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t packed) {
-  return __uint_as_float(packed & 0xFFFF0000u);
-}
-
-// SiLU in fp32 with the full-precision exponential and an IEEE division.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
 // ---- routing/align tables carved from the workspace ------------------------------------------
 struct AlignTables {
@@ -52,6 +29,14 @@ struct AlignTables {
 
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Sizes shared by the kernels and the host-side dispatch rules (host_rules.cpp), which is plain C++
+// so the dispatcher and validation also build without the GPU compiler (sanitizer checks).
+constexpr int kSmallBlockRows = 16;      // rows of a moe_align block for the streaming GEMMs
+constexpr int kPipeBlockRows = 320;      // ... and for the LDS-tiled GEMMs (bf16 and FP8)
+constexpr int kRouterChunk = 256;        // hidden chunk of the partial-logit and one-pass routers
+constexpr int kRouterMaxChunks = 32;     // most hidden chunks the partial-logit selection sums
+constexpr int kBoundaryMaxHidden = 16 * 4 * 256;   // widest row of the boundary kernel
 
 // Upper bound on the number of row blocks when every expert's rows are split into ceil(c/BM)
 // blocks: sum_e ceil(c_e/BM) <= floor(TK/BM) + min(E, TK) + 1.
@@ -132,6 +117,10 @@ hipError_t launch_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, const float*
                                 int64_t n, hipStream_t st);
 int small_block_rows();
 int tiled_block_rows(bool fp8);   // rows per block of the tiled GEMMs
+// Device address of this GPU's 64 MiB workspace array of the no-allocation entry point (scratch.hip),
+// looked up once per device; hipSuccess or the lookup's error.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_of_current_device(void** out);
 // post-norm -> depth-scaled residual -> next pre-norm (boundary.hip)
 struct BoundaryArgs {
   const uint16_t* h;         // [T][H] bf16 residual stream in

@@ -10,7 +10,7 @@
 //   any hardware conversion mode; the sign of zero follows the input (-0 -> 0x80).
 #include <algorithm>
 
-#include "common.h"
+#include "device_common.h"
 
 namespace beam {
 

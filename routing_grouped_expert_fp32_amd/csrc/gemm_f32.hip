@@ -3,7 +3,7 @@
 // Same block structure as the bf16 path (rows grouped per expert by moe_align), one thread per
 // (row, output column), FP32 fused multiply-adds along the contracted dimension.
 // SwiGLU without biases: [H] "Reflection 发布 501B 开源模型 Beam，Apache 2.0 许可" §专家混合.
-#include "common.h"
+#include "device_common.h"
 
 namespace beam {
 

@@ -16,14 +16,15 @@
 //     direct loads.
 #include <algorithm>
 
-#include "common.h"
+#include "device_common.h"
 #include "gemm_pipe.h"
 #include "gemm_small.h"
 
 namespace beam {
 
-int small_block_rows() { return kSmallBM; }
-int tiled_block_rows(bool fp8) { return fp8 ? PipeCfg<true>::BM : PipeCfg<false>::BM; }
+static_assert(kSmallBM == kSmallBlockRows, "block rows of the streaming GEMMs");
+static_assert(PipeCfg<false>::BM == kPipeBlockRows && PipeCfg<true>::BM == kPipeBlockRows,
+              "block rows of the tiled GEMMs");
 
 template <bool GATE_UP, bool FP8>
 static void launch_one(const void* a, const void* w, void* out,
@@ -92,25 +93,5 @@ hipError_t launch_down(const void* h, const void* w_dn, const float* h_scale, co
   return hipGetLastError();
 }
 
-int down_ksplit(int64_t tiles, int64_t k_stages, int n_cu) {
-  // Workgroups run one per CU, dealt to the 8 XCDs in contiguous ranges; a grid whose last round
-  // is nearly empty leaves most CUs idle for one workgroup's time. Choose the K split (1, 2 or 4)
-  // with the fewest rounds per unit of work, charging each extra part a little for its partial-sum
-  // traffic; parts keep at least 16 stages.
-  const int64_t cu_per_xcd = std::max(1, n_cu / 8);
-  int best = 1;
-  double best_cost = 1e30;
-  for (int ks = 1; ks <= 4; ks *= 2) {
-    if (k_stages % ks != 0 || k_stages / ks < 16) continue;
-    const int64_t per_xcd = ceil_div(tiles * ks, 8);
-    const double rounds = (double)ceil_div(per_xcd, cu_per_xcd);
-    const double cost = rounds / ks + 0.05 * (ks - 1);
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = ks;
-    }
-  }
-  return best;
-}
 
 }  // namespace beam

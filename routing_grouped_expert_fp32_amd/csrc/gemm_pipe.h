@@ -34,7 +34,7 @@
 #pragma once
 #include <type_traits>
 
-#include "common.h"
+#include "device_common.h"
 
 namespace beam {
 

@@ -14,7 +14,7 @@
 // Y[slot] = topk_w[slot] * y (FP32); FP8 accumulators are dequantised (token/row scale x output-
 // channel scale) first.
 #pragma once
-#include "common.h"
+#include "device_common.h"
 
 namespace beam {
 

@@ -10,7 +10,7 @@
 // group ranks by counting, then K rounds of a wave-wide argmax (xor butterfly) over the kept groups'
 // members. Ties go to the lower group / expert index.
 #pragma once
-#include "common.h"
+#include "device_common.h"
 
 namespace beam {
 

@@ -15,7 +15,7 @@
 //   workgroups (a handful of tokens would leave W_r streamed by a few CUs); partial logits are
 //   summed in chunk order by the selection.
 // router_select: one wave per token, no sort (route_select.h).
-#include "common.h"
+#include "device_common.h"
 #include "route_select.h"
 
 namespace beam {
@@ -376,10 +376,7 @@ __global__ __launch_bounds__(64 * kRfWaves, 1) void router_fused_kernel(
   }
 }
 
-bool use_fused_router(const Shape& s, bool x_bf16) {
-  return x_bf16 && s.T > kSmallRouteT && s.E <= 256 && s.E % 16 == 0 && s.H % kRfChunk == 0 &&
-         s.G <= 64 && s.K <= 64;
-}
+static_assert(kRfChunk == kRouterChunk && kMaxChunks == kRouterMaxChunks, "router chunking");
 
 hipError_t launch_router_split(const float* w_router, uint16_t* planes, const Shape& s,
                                hipStream_t st) {
@@ -451,12 +448,6 @@ hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const 
   hipLaunchKernelGGL(router_select_kernel<ScoresFromPairs>, grid, dim3(256), 0, st,
                      ScoresFromPairs{sb, s.E}, ids, w, s.T, s.E, s.G, s.Gk, s.K, s.scale);
   return hipGetLastError();
-}
-
-int router_partial_chunks(const Shape& s) { return s.H / 256; }
-
-bool use_small_route(const Shape& s) {
-  return s.T <= kSmallRouteT && router_partial_chunks(s) <= kMaxChunks;
 }
 
 hipError_t launch_router_select_partials(const float* part, const float* bias, int32_t* ids,

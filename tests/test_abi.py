@@ -320,3 +320,46 @@ def test_workspace_region_and_convert_validation():
     assert lib.beam_moe_convert(A[0], 16, bm.BEAM_BF16, A[0] + 16, None) == ALIAS
     if not _gpu_visible():
         assert lib.beam_moe_convert(A[0], 16, bm.BEAM_FP8_E4M3, A[1], None) == DEVICE
+
+
+HOSTCHECK = os.path.join(os.path.dirname(__file__), "hostcheck")
+CSRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "routing_grouped_expert_fp32_amd",
+                    "csrc")
+
+
+@pytest.fixture(scope="module")
+def hostcheck_binary(tmp_path_factory):
+    """The host dispatcher and validation (api.cpp, host_rules.cpp) built for the CPU with
+    AddressSanitizer and UndefinedBehaviorSanitizer, linked against stubs of the HIP runtime and of
+    every kernel launcher (tests/hostcheck/stubs.cpp); no GPU code is built or run."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("hostcheck") / "hostcheck")
+    srcs = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "host_rules.cpp"),
+            os.path.join(HOSTCHECK, "stubs.cpp"), os.path.join(HOSTCHECK, "driver.cpp")]
+    sanitizers = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-Wall", "-fno-omit-frame-pointer", *sanitizers,
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", *srcs, "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-4000:]
+    return exe
+
+
+@pytest.mark.parametrize("mode", ["plain", "sync"])
+def test_host_dispatch_under_sanitizers(hostcheck_binary, mode):
+    """Every entry point over 7 cfgs x 13 batch sizes (0 .. 32768) plus the dense layer, with each
+    launch's buffers checked against the arguments and the workspace, and the validation errors,
+    under ASan/UBSan; `sync` runs with BEAM_MOE_SYNC_CHECK=1 (one stream synchronisation per
+    launch)."""
+    import subprocess
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    env.pop("BEAM_MOE_SYNC_CHECK", None)
+    args = [hostcheck_binary] + (["--sync"] if mode == "sync" else [])
+    res = subprocess.run(args, capture_output=True, text=True, timeout=600, env=env)
+    assert res.returncode == 0, (res.stdout[-2000:], res.stderr[-4000:])
+    m = re.search(r"hostcheck: (\d+) checks, 0 failed, (\d+) launches checked", res.stdout)
+    assert m and int(m.group(2)) > 1000, res.stdout
