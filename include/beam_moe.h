@@ -107,7 +107,7 @@ typedef struct beam_moe_cfg {
  *   topk_w    [T][K] fp32 out — routed_scale * s_k / sum_j s_j, s = sigmoid(logit) (unbiased)
  *   workspace device scratch of at least beam_moe_route_workspace_bytes(cfg, T) bytes
  * Ties between equal FP32 scores (groups or experts) go to the lower index.
- * Logits are FP32 sums of exact products. With bf16 x and T > 64 each FP32 router weight is split
+ * Logits are FP32 sums of exact products. With bf16 x and T > 1024 each FP32 router weight is split
  * exactly into three bf16 terms (valid for |w| >= 2^-102; smaller weights lose only bits below
  * 2^-126), written to the workspace, and the bf16 matrix cores accumulate the products in FP32;
  * otherwise the FP32 matrix cores multiply x (widened to FP32 if bf16) by the weights directly. */
@@ -326,7 +326,7 @@ BEAM_API int32_t beam_moe_version(void);
  * returns the number of stages defined. Stage order: 0 router logits, 1 router select,
  * 2 moe_align, 3 activation quant (fp8), 4 gate/up GEMM, 5 h quant (fp8), 6 down GEMM,
  * 7 combine (for forwards of up to 16 tokens the selection and the align are one launch, recorded
- * as stage 1; past 64 tokens with bf16 activations the logits and the selection are one launch,
+ * as stage 1; past 1024 tokens with bf16 activations the logits and the selection are one launch,
  * recorded as stage 0 together with the split of the router weights that precedes it). beam_moe_stage_name(i) names stage i.
  * beam_moe_timing_stages(mask) restricts the recording to the stages whose bit (1 << stage) is set
  * (default: all), so a caller can time one kernel without event records between the others. */

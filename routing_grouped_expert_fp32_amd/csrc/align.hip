@@ -182,10 +182,10 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------------------------
-// Small batches (T <= kSmallRouteT = 64 tokens): the whole align in one workgroup of 1024 threads.
+// Small batches (T <= kSmallAlignT = 64 tokens): the whole align in one workgroup of 1024 threads.
 // One 64-bit mask per expert (bit t: token t chose it), counts by popcount, exclusive scans over the
 // experts in LDS, the same block table and the same stable token order as the three-kernel path.
-static_assert(kSmallRouteT <= 64, "one mask word per expert");
+static_assert(kSmallAlignT <= 64, "one mask word per expert");
 
 __device__ void align_small_body(const int32_t* sid, const float* tw, int64_t T, int E, int K,
                                  int e_begin, int BM, const AlignTables& at) {
@@ -267,8 +267,8 @@ __global__ __launch_bounds__(1024) void select_align_small_kernel(ScoresFromPart
                                                                   int BM) {
   __shared__ float bl[16][256];
   __shared__ float gsc[16][64];
-  __shared__ int32_t sid[kSmallRouteT * 16];
-  __shared__ float sw[kSmallRouteT * 16];
+  __shared__ int32_t sid[kSmallAlignT * 16];
+  __shared__ float sw[kSmallAlignT * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int64_t t = wave; t < T; t += 16) {
     int id;
@@ -317,7 +317,7 @@ hipError_t launch_fill_dense_routes(int32_t* ids, float* w, int64_t n, hipStream
 hipError_t launch_align(const int32_t* ids, const float* topk_w, const AlignTables& at,
                         const Shape& s, int BM, int e_begin, int e_count, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
-  if (s.T <= kSmallRouteT) {
+  if (s.T <= kSmallAlignT) {
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, st, ids, topk_w, at, s.T,
                        e_count, s.K, e_begin, BM);
     return hipGetLastError();

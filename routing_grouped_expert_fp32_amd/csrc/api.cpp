@@ -50,7 +50,7 @@ int block_rows(const beam_moe_cfg& c, int64_t T) {
 struct Layout {
   size_t sb = 0, ids = 0, w = 0, chunk_mask = 0, chunk_base = 0, expert_count = 0, expert_off = 0,
          n_blocks = 0, blk_expert = 0, blk_row0 = 0, blk_rows = 0, sorted = 0, sorted_w = 0, hbuf = 0,
-         ybuf = 0, xq = 0, xs = 0, hq = 0, hs = 0, wsplit = 0, total = 0;
+         ybuf = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
   int64_t max_blocks = 0;
   int bm = 0;
 };
@@ -65,20 +65,19 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full, int ybuf_parts =
     return o;
   };
   const int64_t E = c.n_experts, K = c.topk, TK = T * K;
-  // small batches: the partial logits [H/256][T][E]; larger ones with bf16 activations: the router
-  // weights split into three bf16 planes, 3 E H values (in a forward they share the region of the
-  // expert outputs, which are written only after the routing); otherwise (s, b) pairs [T][E]
-  const bool split_route = c.x_dtype == BEAM_BF16 && T > beam::kSmallRouteT;
-  const size_t split_bytes = split_route ? 6 * (size_t)E * (size_t)c.hidden : 0;
-  size_t sb_bytes;
-  if (T <= beam::kSmallRouteT)
-    sb_bytes = sizeof(float) * (size_t)(std::max<int64_t>(2, c.hidden / 256) * T * E);
-  else if (split_route)
-    sb_bytes = full ? 16 : split_bytes;
+  // Router scratch: the partial logits [H/256][T][E] (partial path), the router weights split into
+  // three bf16 planes, 3 E H values (one-pass router), or (s, b) pairs [T][E]. In a forward it
+  // shares the region of the expert outputs, which are written only after the routing.
+  const beam::Shape s{T, c.hidden, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.d_ff,
+                      c.routed_scale};
+  size_t route_bytes;
+  if (beam::use_partial_route(s))
+    route_bytes = sizeof(float) * (size_t)beam::router_partial_chunks(s) * (size_t)(T * E);
+  else if (beam::use_fused_router(s, c.x_dtype == BEAM_BF16))
+    route_bytes = 6 * (size_t)E * (size_t)c.hidden;
   else
-    sb_bytes = sizeof(float) * (size_t)(2 * T * E);
-  L.sb = take(sb_bytes);
-  L.wsplit = L.sb;
+    route_bytes = sizeof(float) * (size_t)(2 * T * E);
+  if (!full) L.sb = take(route_bytes);
   if (full) {
     const int64_t n_chunks = ceil_div(T, beam::kAlignChunk);
     L.bm = block_rows(c, T);
@@ -105,8 +104,8 @@ Layout make_layout(const beam_moe_cfg& c, int64_t T, bool full, int ybuf_parts =
     }
     // last, so the offsets above do not depend on the number of partial rows per slot
     L.ybuf = take(std::max(sizeof(float) * (size_t)TK * (size_t)ybuf_parts * (size_t)c.hidden,
-                           split_bytes));
-    if (split_route) L.wsplit = L.ybuf;
+                           route_bytes));
+    L.sb = L.ybuf;
   }
   L.total = off;
   return L;
@@ -329,16 +328,19 @@ beam_status_t run_experts(const beam_moe_cfg& c, int64_t T, const Layout& L, cha
   return BEAM_OK;
 }
 
-// Routing of a batch past the small-batch path: bf16 activations take the one-pass router
-// (logits and selection in one launch), FP32 ones the logits kernel and then the selection.
+// Routing of a batch past the partial-logit path: bf16 activations take the one-pass router
+// (weight split, then logits and selection in one launch), FP32 ones the logits kernel and then the
+// selection. `scratch` is the router scratch region of the workspace.
 beam_status_t route_large(const void* x, bool x_bf16, const float* w_router, const float* bias,
-                          float2* sb, uint16_t* wsplit, int32_t* ids, float* tw,
-                          const beam::Shape& s, hipStream_t st) {
+                          char* scratch, int32_t* ids, float* tw, const beam::Shape& s,
+                          hipStream_t st) {
   if (beam::use_fused_router(s, x_bf16)) {
-    LAUNCH(0, beam::launch_router_split(w_router, wsplit, s, st));
-    LAUNCH(0, beam::launch_router_fused(x, wsplit, bias, ids, tw, s, st));
+    uint16_t* planes = reinterpret_cast<uint16_t*>(scratch);
+    LAUNCH(0, beam::launch_router_split(w_router, planes, s, st));
+    LAUNCH(0, beam::launch_router_fused(x, planes, bias, ids, tw, s, st));
     return BEAM_OK;
   }
+  float2* sb = reinterpret_cast<float2*>(scratch);
   LAUNCH(0, beam::launch_router_logits(x, x_bf16, w_router, bias, sb, s, st));
   LAUNCH(1, beam::launch_router_select(sb, ids, tw, s, st));
   return BEAM_OK;
@@ -454,11 +456,10 @@ beam_status_t forward_impl(const void* x, const float* w_router, const float* bi
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
   float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
   const beam::Shape s = shape_of(c, T);
-  if (beam::use_small_route(s)) {   // partial logits, selection summing them
+  if (beam::use_partial_route(s)) {   // partial logits, selection summing them
     float* part = reinterpret_cast<float*>(ws + L.sb);
     LAUNCH(0, beam::launch_router_partials(x, c.x_dtype == BEAM_BF16, w_router, part, s, st));
     if (beam::use_fused_select_align(s)) {   // the selection and the align in one launch
@@ -468,9 +469,8 @@ beam_status_t forward_impl(const void* x, const float* w_router, const float* bi
                          w_down_scale, out, 0, c.n_experts, false, st, nullptr, 1, true);
     }
     LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
-  } else if ((rc = route_large(x, c.x_dtype == BEAM_BF16, w_router, bias, sb,
-                               reinterpret_cast<uint16_t*>(ws + L.wsplit), ids, tw, s, st)) !=
-             BEAM_OK) {
+  } else if ((rc = route_large(x, c.x_dtype == BEAM_BF16, w_router, bias, ws + L.sb, ids, tw, s,
+                               st)) != BEAM_OK) {
     return rc;
   }
   return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
@@ -580,16 +580,15 @@ beam_status_t beam_moe_route(const void* x, const float* w_router, const float* 
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
   const beam::Shape s = shape_of(c, T);
-  if (beam::use_small_route(s)) {
+  if (beam::use_partial_route(s)) {
     float* part = reinterpret_cast<float*>(ws + L.sb);
     LAUNCH(0, beam::launch_router_partials(x, c.x_dtype == BEAM_BF16, w_router, part, s, st));
     LAUNCH(1, beam::launch_router_select_partials(part, bias, topk_ids, topk_w, s, st));
     return BEAM_OK;
   }
-  return route_large(x, c.x_dtype == BEAM_BF16, w_router, bias, sb,
-                     reinterpret_cast<uint16_t*>(ws + L.wsplit), topk_ids, topk_w, s, st);
+  return route_large(x, c.x_dtype == BEAM_BF16, w_router, bias, ws + L.sb, topk_ids, topk_w, s,
+                     st);
 }
 
 beam_status_t beam_moe_forward(const void* x, const float* w_router, const float* bias,
@@ -698,11 +697,10 @@ beam_status_t beam_moe_forward_boundary(const void* x, const float* w_router, co
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  float2* sb = reinterpret_cast<float2*>(ws + L.sb);
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
   float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
   const beam::Shape s = shape_of(c, T);
-  if (beam::use_small_route(s)) {
+  if (beam::use_partial_route(s)) {
     float* part = reinterpret_cast<float*>(ws + L.sb);
     LAUNCH(0, beam::launch_router_partials(x, true, w_router, part, s, st));
     if (beam::use_fused_select_align(s)) {   // as in beam_moe_forward
@@ -712,9 +710,7 @@ beam_status_t beam_moe_forward_boundary(const void* x, const float* w_router, co
                          w_down_scale, nullptr, 0, c.n_experts, false, st, &bnd, 1, true);
     }
     LAUNCH(1, beam::launch_router_select_partials(part, bias, ids, tw, s, st));
-  } else if ((rc = route_large(x, true, w_router, bias, sb,
-                               reinterpret_cast<uint16_t*>(ws + L.wsplit), ids, tw, s, st)) !=
-             BEAM_OK) {
+  } else if ((rc = route_large(x, true, w_router, bias, ws + L.sb, ids, tw, s, st)) != BEAM_OK) {
     return rc;
   }
   return run_experts(c, T, L, ws, ids, tw, x, w_gate_up, w_down, w_gate_up_scale, w_down_scale,

@@ -57,18 +57,23 @@ struct Shape {
 
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_router,
                                 const float* bias, float2* sb, const Shape& s, hipStream_t st);
-// batches of at most this many tokens take the small-batch routing path (use_small_route): partial
-// logits split over 256-wide hidden chunks, selection summing them, align in one workgroup
-constexpr int64_t kSmallRouteT = 64;
+// Batches of at most kPartialRouteT tokens are routed through partial logits split over 256-wide
+// hidden chunks (many workgroups stream W_r; the selection sums the chunks in order); larger ones
+// take the one-pass router with bf16 activations (use_fused_router), else the logits kernel and
+// the selection. Its time barely grows with T (each workgroup streams all of W_r once), the partial
+// path's grows linearly: they cross near 1100 tokens at Beam's shape.
+constexpr int64_t kPartialRouteT = 1024;
+// batches of at most kSmallAlignT tokens are aligned by one workgroup
+constexpr int64_t kSmallAlignT = 64;
 int router_partial_chunks(const Shape& s);
-bool use_small_route(const Shape& s);
+bool use_partial_route(const Shape& s);
 hipError_t launch_router_partials(const void* x, bool x_bf16, const float* w_router, float* part,
                                   const Shape& s, hipStream_t st);
 hipError_t launch_router_select_partials(const float* part, const float* bias, int32_t* ids,
                                          float* w, const Shape& s, hipStream_t st);
 hipError_t launch_router_select(const float2* sb, int32_t* ids, float* w, const Shape& s,
                                 hipStream_t st);
-// bf16 activations and T > kSmallRouteT: the router weights split exactly into three bf16 planes
+// bf16 activations past the partial path: the router weights split exactly into three bf16 planes
 // (3 E H bf16, in MFMA fragment order; launch_router_split), then logits and selection in one
 // launch with no HBM round trip
 bool use_fused_router(const Shape& s, bool x_bf16);
@@ -83,7 +88,7 @@ hipError_t launch_align(const int32_t* ids, const float* topk_w, const AlignTabl
 // of one workgroup (a wave per token; larger small batches select over many workgroups first)
 constexpr int64_t kFusedSelectT = 16;
 inline bool use_fused_select_align(const Shape& s) {
-  return s.T <= kFusedSelectT && s.K <= 16 && s.T <= kSmallRouteT;
+  return s.T <= kFusedSelectT && s.K <= 16 && s.T <= kSmallAlignT && use_partial_route(s);
 }
 hipError_t launch_select_align_small(const float* part, const float* bias, int32_t* ids, float* w,
                                      const AlignTables& at, const Shape& s, int BM, hipStream_t st);

@@ -12,12 +12,12 @@ int boundary_max_hidden() { return kBoundaryMaxHidden; }
 
 int router_partial_chunks(const Shape& s) { return s.H / kRouterChunk; }
 
-bool use_small_route(const Shape& s) {
-  return s.T <= kSmallRouteT && router_partial_chunks(s) <= kRouterMaxChunks;
+bool use_partial_route(const Shape& s) {
+  return s.T <= kPartialRouteT && router_partial_chunks(s) <= kRouterMaxChunks;
 }
 
 bool use_fused_router(const Shape& s, bool x_bf16) {
-  return x_bf16 && s.T > kSmallRouteT && s.E <= 256 && s.E % 16 == 0 &&
+  return x_bf16 && !use_partial_route(s) && s.E <= 256 && s.E % 16 == 0 &&
          s.H % kRouterChunk == 0 && s.G <= 64 && s.K <= 64;
 }
 

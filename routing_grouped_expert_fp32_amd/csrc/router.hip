@@ -25,7 +25,7 @@ namespace beam {
 // Per 16-wide K step a lane loads 4 consecutive K values of one token row (A) and of one expert
 // row (B); MFMA step c consumes component c, so step c sums K offsets {c, 4+c, 8+c, 12+c}: the same
 // permutation on both operands, hence the same products.
-// Tiles for T > 64: 64 tokens x 64 experts (each workgroup reads its 1.3 MB W_r slice for twice
+// Tiles past 64 tokens: 64 tokens x 64 experts (each workgroup reads its 1.3 MB W_r slice for twice
 // as many tokens as with 32-token tiles: 0.275 -> 0.225 ms at T=8192, 1.03 -> 0.845 ms at
 // T=32768), two workgroups per CU by registers and LDS; 128-token tiles spill. Loading the next
 // 16-deep step's operands ahead of the current MFMAs measured slower.
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256, TM >= 64 ? 2 : 4) void router_logits_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Logits for small batches (T <= kSmallRouteT): split over the hidden dimension so that enough
+// Logits for small batches (T <= kPartialRouteT): split over the hidden dimension so that enough
 // workgroups stream W_r. WG (token tile of 16, expert tile of 16, hidden chunk of 256); wave w takes
 // hidden [256 q + 64 w, 256 q + 64 w + 64), the four wave partials are summed in wave order and
 // written to part[q][t][e]; the selection sums the chunks q in order.
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const void* __restr
 }
 
 // ---------------------------------------------------------------------------------------------
-// One-pass router for bf16 activations (T > kSmallRouteT): logits, sigmoid, bias and selection in
+// One-pass router for bf16 activations (T > kPartialRouteT): logits, sigmoid, bias and selection in
 // one workgroup per 32 tokens; the logits never leave the chip.
 //
 // Exact split of the FP32 weights, once per call (router_split_kernel): w = hi + mid + lo with three

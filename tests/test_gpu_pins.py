@@ -41,7 +41,7 @@ def _route_exact(x, w_r, bias):
     return ids.cpu().numpy(), w.cpu().numpy(), r
 
 
-@pytest.mark.parametrize("T", [5, 100])
+@pytest.mark.parametrize("T", [5, 100, 1100])
 def test_all_ties(T):
     """W_r = 0, bias = 0: every expert scores 1/2, so groups 0-3 and experts 0-7 are chosen, in
     index order, each with weight 2.5 / 8."""
@@ -54,11 +54,12 @@ def test_all_ties(T):
     assert (r.ids == np.arange(8)[None, :]).all()
 
 
-@pytest.mark.parametrize("T", [5, 100])
+@pytest.mark.parametrize("T", [5, 100, 1100])
 def test_planted_ties_on_an_exact_grid(T):
     """W_r = 0 and biases drawn from a handful of values on a 2^-10 grid: many equal scores inside
     and across groups and equal group scores; the GPU's ids must equal the oracle's exactly, in
-    order, for 24 different bias vectors (the T <= 64 and the T > 64 routing paths)."""
+    order, for 24 different bias vectors (the fused select-and-align launch, the partial-logit path
+    and the one-pass router)."""
     x = synthgen.normal((T, SH.hidden), 1.0, 0, 1, "cuda", torch.bfloat16)
     w_r = torch.zeros((SH.n_experts, SH.hidden), dtype=torch.float32, device="cuda")
     rng = np.random.default_rng(T)
@@ -76,7 +77,7 @@ def test_planted_ties_on_an_exact_grid(T):
     assert n_group_ties > 0
 
 
-@pytest.mark.parametrize("T", [40, 200])
+@pytest.mark.parametrize("T", [40, 200, 1100])
 def test_ties_from_identical_router_rows(T):
     """Real scores with planted ties: groups 1 and 5 are copies of group 0 (equal group scores), and
     inside groups 2 and 6 every even expert's router row is copied to the next one. The GPU must pick

@@ -35,7 +35,8 @@ def _case(w_dtype, T):
     return run, out, ids
 
 
-@pytest.mark.parametrize("w_dtype,T", [("bf16", 8), ("bf16", 700), ("fp8", 700)])
+@pytest.mark.parametrize("w_dtype,T",
+                         [("bf16", 8), ("bf16", 700), ("fp8", 700), ("bf16", 1100)])
 def test_graph_replay_equals_eager(w_dtype, T):
     print("graph capture", w_dtype, "T =", T, flush=True)
     run, out, ids = _case(w_dtype, T)
@@ -86,9 +87,9 @@ def test_timing_stage_mask():
     st = bm.timing_collect()
     for k in ("router_logits", "router_select", "moe_align", "gate_up", "down", "combine"):
         assert st[k][1] == 1, (k, st)
-    # past 64 tokens bf16 activations take the one-pass router, after the split of the router
+    # past 1024 tokens bf16 activations take the one-pass router, after the split of the router
     # weights (both recorded as router_logits)
-    run3, _, _ = _case("bf16", 100)
+    run3, _, _ = _case("bf16", 1100)
     bm.timing_enable(True)
     run3()
     torch.cuda.synchronize()
