@@ -54,7 +54,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
-KERNEL_SOURCES = ("gemm_grouped.hip", "gemm_pipe.h", "gemm_small.h", "common.h")
+KERNEL_SOURCES = ("gemm_grouped.hip", "gemm_pipe.h", "gemm_small.h", "common.h",
+                  "device_common.h")
 
 
 def kernel_source_hash() -> str:
@@ -470,7 +471,114 @@ def measure_small_t(bm, synthgen, torch, weights, steps, warmup, Ts=(1, 2, 4, 8,
     return res
 
 
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> None:
+    """Writes profiles/counters_<workload>.{json,txt} from two rocprofv3 --pmc runs of this script
+    (FETCH_SIZE, then WRITE_SIZE, each with --copy-probe-gib 1): per-kernel KiB per dispatch averaged
+    over the run's dispatches, scaled to bytes by what the same counter reads for the 1 GiB device
+    copy (read once, written once)."""
+    import csv
+    import collections
+
+    def dispatches(d, counter):
+        vals = collections.defaultdict(list)
+        for root, _, files in os.walk(d):
+            for fn in files:
+                if fn.endswith("counter_collection.csv"):
+                    with open(os.path.join(root, fn)) as f:
+                        for r in csv.DictReader(f):
+                            if r["Counter_Name"] == counter:
+                                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fd, wd = dispatches(fetch_dir, "FETCH_SIZE"), dispatches(write_dir, "WRITE_SIZE")
+    fetch = {k: sum(v) / len(v) for k, v in fd.items()}
+    write = {k: sum(v) / len(v) for k, v in wd.items()}
+    # the probe is the largest copy dispatch (smaller copies of the run share its kernel)
+    copy = [k for k in fd if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no copy-probe dispatch in the FETCH_SIZE run (--copy-probe-gib 1)")
+    probe = 2 ** 30
+    f_copy = max(max(fd[k]) for k in copy)
+    w_copy = max(max(wd.get(k, [0.0])) for k in copy)
+    fs, ws = probe / (1024 * f_copy), probe / (1024 * w_copy)
+    short = {}
+    for k in fetch:
+        if "beam::" in k:
+            name = k.split("(")[0].replace("void ", "")
+            short[name] = {"FETCH_SIZE_KiB": fetch[k], "WRITE_SIZE_KiB": write.get(k, 0.0),
+                           "hbm_bytes": 1024 * (fs * fetch[k] + ws * write.get(k, 0.0))}
+    gu = [n for n in short if n.startswith("beam::grouped_") and "<true" in n]
+    out = {"workload": workload, "kernel": gu[0] if gu else None,
+           "kernel_source_hash": kernel_source_hash(), "fetch_scale": fs, "write_scale": ws,
+           "copy_probe": {"bytes": probe, "FETCH_SIZE_KiB": f_copy, "WRITE_SIZE_KiB": w_copy},
+           "gate_up_hbm_bytes_per_launch": short[gu[0]]["hbm_bytes"] if gu else None,
+           "per_kernel": short}
+    base = os.path.join(ROOT, "profiles", f"counters_{workload}")
+    with open(base + ".json", "w") as f:
+        json.dump(out, f, indent=1)
+    cmd = ('rocprofv3 --pmc {c} --kernel-include-regex "beam::|copyBuffer" --output-format csv '
+           '-d $R/gpurun_out/pmc_{w}_{c} -o run -- python $R/bench.py --workload {w} --also "" '
+           '--steps 3 --warmup 1 --no-cpu-baseline --no-ceilings --copy-probe-gib 1')
+    lines = [f"# HBM traffic per dispatch from rocprofv3 counters, workload {workload}", "",
+             "commands (from /tmp with TMPDIR=/tmp, repository root $R; one pass per counter):",
+             "  " + cmd.format(c="FETCH_SIZE", w=workload),
+             "  " + cmd.format(c="WRITE_SIZE", w=workload),
+             f"summary: python $R/bench.py --summarize-counters {workload} "
+             f"$R/gpurun_out/pmc_{workload}_FETCH_SIZE $R/gpurun_out/pmc_{workload}_WRITE_SIZE", "",
+             f"copy probe (device copy of 1 GiB = 1048576 KiB): FETCH_SIZE {f_copy:.1f} KiB, "
+             f"WRITE_SIZE {w_copy:.1f} KiB", f"-> scale factors: FETCH x{fs:.4f}, WRITE x{ws:.4f}",
+             "", f"{'kernel':<55}{'FETCH_KiB':>13}{'WRITE_KiB':>13}{'HBM_bytes(scaled)':>19}"]
+    for n, v in short.items():
+        lines.append(f"{n[:54]:<55}{v['FETCH_SIZE_KiB']:>13.1f}{v['WRITE_SIZE_KiB']:>13.1f}"
+                     f"{v['hbm_bytes']:>19.4g}")
+    with open(base + ".txt", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {base}.json / .txt")
+
+
+def summarize_trace(trace_dir: str) -> None:
+    """Writes profiles/kernels_bench_all_workloads.txt from the kernel_stats.csv of
+    `rocprofv3 --kernel-trace --stats --output-format csv` over a default bench.py run: the library's
+    kernels with their call counts and average / min / max durations."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(trace_dir):
+        for fn in files:
+            if fn.endswith("kernel_stats.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    rows += [r for r in csv.DictReader(f) if "beam::" in r["Name"]]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [
+        "# rocprofv3 kernel-trace stats: bench.py default run (decode T=32 headline; legs prefill",
+        "# T=8192, skew T=32768, fp8_decode T=32, fp8_prefill T=8192, routed_prefill (experts",
+        "# 32..63 of the T=8192 batch), dense_prefill (dense SwiGLU d_ff 20480, T=8192),",
+        "# boundary_prefill (post-MoE boundary, T=8192), small_t (T = 1 .. 64))", "",
+        "command (from /tmp with TMPDIR=/tmp, repository root $R):",
+        "  rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_all -o all "
+        "-- python $R/bench.py",
+        "summary: python $R/bench.py --summarize-trace $R/gpurun_out/prof_all", "",
+        "Template arguments: grouped_*<GATE_UP, FP8, ...>: <true,*> gate/up, <false,*> down;",
+        "small_ks = 16-row blocks, K split across 8 or 4 waves (decode legs); pipe = 320-row blocks",
+        "(prefill legs). router_fused_kernel (with router_split_kernel before it): the one-pass router",
+        "past 1024 tokens; router_partial_kernel + select: up to 1024 tokens.", "",
+        f"{'kernel':<62}{'calls':>8}{'avg_us':>11}{'min_us':>11}{'max_us':>11}"]
+    for r in rows:
+        name = r["Name"].replace("void ", "").split("(")[0]
+        lines.append(f"{name[:61]:<62}{int(r['Calls']):>8}{float(r['AverageNs']) / 1e3:>11.1f}"
+                     f"{float(r['MinNs']) / 1e3:>11.1f}{float(r['MaxNs']) / 1e3:>11.1f}")
+    out = os.path.join(ROOT, "profiles", "kernels_bench_all_workloads.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        summarize_counters(*sys.argv[2:5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2])
+        return
     a = parse()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the library has no "

@@ -68,8 +68,8 @@ struct PipeCfg {
 // 8 ways in the XCD's L2
 constexpr int kPGroup = 4;
 
-// cache-policy operand of the direct loads: non-temporal for the weight stream (a weight tile is
-// read once per row block of its expert, so it should not push the shared token rows out of L2)
+// cache-policy operand of the direct loads: non-temporal for the weight stream of a one-block
+// expert (its weight tile is read once, so it should not push the shared token rows out of L2)
 constexpr int kCachePolicyNT = 2;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -155,6 +155,7 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
   // XCD and that tile streams from HBM about once per group instead of once per block. A
   // one-block group is walked as before (its column tiles in order, sharing the token rows).
   int b, j;
+  bool shared_w;   // the tile's weight stages are read by other blocks of its group too
   {
     const int bn = vt / n_ctiles;                        // block in natural (column-fastest) order
     const int en = at.blk_expert[bn];
@@ -166,6 +167,7 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
     const int off = vt - (bn - (ib - g0)) * n_ctiles;   // tile within the group
     j = off / sz;
     b = bn - (ib - g0) + off % sz;
+    shared_w = sz > 1;
   }
   const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
 
@@ -214,14 +216,23 @@ __global__ __launch_bounds__(64 * PipeCfg<FP8>::WAVES, 1) void grouped_pipe_kern
       __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[q] + kb),
                                        (lds_void_t*)(base + (wave * LA + q) * 1024), 16, 0, 0);
   };
+  // weight stages read by one block only stream past L2 (non-temporal); those a group shares keep
+  // the default policy, so the group's other blocks find them there
   auto issue_b = [&](int stage) {
     unsigned char* base = bring + (stage % C::BST) * C::kBStageBytes;
     const int kb = stage * kPRowBytes;
+    if (shared_w) {
 #pragma unroll
-    for (int q = 0; q < LB; ++q)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(bsrc + q * bstep + kb),
-                                       (lds_void_t*)(base + (wave * LB + q) * 1024), 16, 0,
-                                       kCachePolicyNT);
+      for (int q = 0; q < LB; ++q)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(bsrc + q * bstep + kb),
+                                         (lds_void_t*)(base + (wave * LB + q) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < LB; ++q)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(bsrc + q * bstep + kb),
+                                         (lds_void_t*)(base + (wave * LB + q) * 1024), 16, 0,
+                                         kCachePolicyNT);
+    }
   };
 
   floatx4 acc[NVMAX][8];
