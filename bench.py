@@ -111,7 +111,7 @@ def timed_steps(bm, torch, step, steps, warmup, stage):
     around `stage` only (one event pair per call on the call's stream, so no event records sit
     between the other kernels); then a second, instrumented pass of the same calls records every
     stage for the breakdown. Returns (ms per step, average ms of `stage` in the timed steps,
-    {stage: average ms} of the instrumented pass)."""
+    {stage: ms per step, summed over its launches} of the instrumented pass)."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -129,7 +129,7 @@ def timed_steps(bm, torch, step, steps, warmup, stage):
         step()
     torch.cuda.synchronize()
     bm.timing_enable(False)
-    stages = {k: (v[0] / v[1] if v[1] else None) for k, v in bm.timing_collect().items()}
+    stages = {k: (v[0] / steps if v[1] else None) for k, v in bm.timing_collect().items()}
     # per-step spread: a third pass with an event pair around every call on the calling stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -536,9 +536,11 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> None:
     print(f"wrote {base}.json / .txt")
 
 
-def summarize_trace(trace_dir: str) -> None:
-    """Writes profiles/kernels_bench_all_workloads.txt from the kernel_stats.csv of
-    `rocprofv3 --kernel-trace --stats --output-format csv` over a default bench.py run: the library's
+def summarize_trace(trace_dir: str, which: str = "all") -> None:
+    """Writes profiles/kernels_bench_all_workloads.txt (which = "all": a default bench.py run) or
+    profiles/kernels_bench_decode.txt (which = "decode": bench.py --also "", the headline decode leg
+    alone, so its gate/up kernel's average can be set beside the bench line's) from the
+    kernel_stats.csv of `rocprofv3 --kernel-trace --stats --output-format csv`: the library's
     kernels with their call counts and average / min / max durations."""
     import csv
     rows = []
@@ -548,15 +550,24 @@ def summarize_trace(trace_dir: str) -> None:
                 with open(os.path.join(root, fn)) as f:
                     rows += [r for r in csv.DictReader(f) if "beam::" in r["Name"]]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    lines = [
-        "# rocprofv3 kernel-trace stats: bench.py default run (decode T=32 headline; legs prefill",
-        "# T=8192, skew T=32768, fp8_decode T=32, fp8_prefill T=8192, routed_prefill (experts",
-        "# 32..63 of the T=8192 batch), dense_prefill (dense SwiGLU d_ff 20480, T=8192),",
-        "# boundary_prefill (post-MoE boundary, T=8192), small_t (T = 1 .. 64))", "",
-        "command (from /tmp with TMPDIR=/tmp, repository root $R):",
-        "  rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_all -o all "
-        "-- python $R/bench.py",
-        "summary: python $R/bench.py --summarize-trace $R/gpurun_out/prof_all", "",
+    if which == "decode":
+        head = ["# rocprofv3 kernel-trace stats: bench.py headline leg only (decode T=32: 5 warm-up",
+                "# + 50 timed steps, 50 instrumented, 50 with an event pair per step, route-only calls)",
+                "", "command (from /tmp with TMPDIR=/tmp, repository root $R):",
+                "  rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_decode "
+                "-o dec -- python $R/bench.py --also \"\" --no-cpu-baseline --no-ceilings",
+                "summary: python $R/bench.py --summarize-trace $R/gpurun_out/prof_decode decode", ""]
+    else:
+        head = [
+            "# rocprofv3 kernel-trace stats: bench.py default run (decode T=32 headline; legs",
+            "# prefill T=8192, skew T=32768, fp8_decode T=32, fp8_prefill T=8192, routed_prefill",
+            "# (experts 32..63 of the T=8192 batch), dense_prefill (dense SwiGLU d_ff 20480,",
+            "# T=8192), boundary_prefill (post-MoE boundary, T=8192), small_t (T = 1 .. 64))", "",
+            "command (from /tmp with TMPDIR=/tmp, repository root $R):",
+            "  rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_all -o all "
+            "-- python $R/bench.py",
+            "summary: python $R/bench.py --summarize-trace $R/gpurun_out/prof_all", ""]
+    lines = head + [
         "Template arguments: grouped_*<GATE_UP, FP8, ...>: <true,*> gate/up, <false,*> down;",
         "small_ks = 16-row blocks, K split across 8 or 4 waves (decode legs); pipe = 320-row blocks",
         "(prefill legs). router_fused_kernel (with router_split_kernel before it): the one-pass router",
@@ -566,7 +577,8 @@ def summarize_trace(trace_dir: str) -> None:
         name = r["Name"].replace("void ", "").split("(")[0]
         lines.append(f"{name[:61]:<62}{int(r['Calls']):>8}{float(r['AverageNs']) / 1e3:>11.1f}"
                      f"{float(r['MinNs']) / 1e3:>11.1f}{float(r['MaxNs']) / 1e3:>11.1f}")
-    out = os.path.join(ROOT, "profiles", "kernels_bench_all_workloads.txt")
+    out = os.path.join(ROOT, "profiles", "kernels_bench_decode.txt" if which == "decode"
+                       else "kernels_bench_all_workloads.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
@@ -577,7 +589,7 @@ def main():
         summarize_counters(*sys.argv[2:5])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
-        summarize_trace(sys.argv[2])
+        summarize_trace(*sys.argv[2:4])
         return
     a = parse()
     if a.gpus != 1:
