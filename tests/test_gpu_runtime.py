@@ -1,6 +1,7 @@
 """Runtime behaviour of the library through the C ABI: a forward step captured in a HIP graph replays
 to the eager result (a call launches kernels on the caller's stream and nothing else: no allocation,
-memset or synchronisation), and the stage-timing mask records only the selected stages."""
+memset or synchronisation), the stage-timing mask records only the selected stages, and the
+BEAM_MOE_SYNC_CHECK debugging mode leaves the results unchanged."""
 import dataclasses
 
 import pytest
@@ -121,3 +122,31 @@ def test_two_streams_with_their_own_workspaces():
             run_b(s2)
         torch.cuda.synchronize()
         assert torch.equal(out_a, ref_a) and torch.equal(out_b, ref_b), f"round {i}"
+
+
+def test_sync_check_mode_gives_the_same_results(tmp_path):
+    """BEAM_MOE_SYNC_CHECK=1 (a stream synchronisation after every launch, failures reported by
+    stage) changes nothing in the results: a child process with it set writes the same bits."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import sys, torch\n"
+        "sys.path.insert(0, sys.argv[1])\n"
+        "import test_gpu_runtime as t\n"
+        "run, out, ids = t._case('bf16', 300)\n"
+        "run(); torch.cuda.synchronize()\n"
+        "torch.save({'out': out.cpu(), 'ids': ids.cpu()}, sys.argv[2])\n")
+    here = os.path.dirname(os.path.abspath(__file__))
+    res = {}
+    for mode in ("0", "1"):
+        path = str(tmp_path / f"sync_{mode}.pt")
+        env = dict(os.environ, BEAM_MOE_SYNC_CHECK=mode,
+                   PYTHONPATH=os.pathsep.join([os.path.dirname(here), here,
+                                               os.environ.get("PYTHONPATH", "")]))
+        r = subprocess.run([sys.executable, "-c", code, here, path], env=env, capture_output=True,
+                           text=True, timeout=240)
+        assert r.returncode == 0, r.stderr[-2000:]
+        res[mode] = torch.load(path, weights_only=True)
+    assert torch.equal(res["0"]["ids"], res["1"]["ids"])
+    assert torch.equal(res["0"]["out"].view(torch.int32), res["1"]["out"].view(torch.int32))
