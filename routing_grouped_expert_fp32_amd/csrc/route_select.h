@@ -7,8 +7,8 @@
 // Grouped MoE Routing (the bias is used to choose only).
 //
 // No sort: lane l owns experts l, l+64, l+128, l+192; group top-2 sums by the group's first lanes,
-// group ranks by counting, then K rounds of a wave-wide argmax (xor butterfly) over the kept groups'
-// members. Ties go to the lower group / expert index.
+// group ranks by counting, then K rounds of a wave-wide argmax (DPP row steps and four lane reads)
+// over the kept groups' members. Ties go to the lower group / expert index.
 #pragma once
 #include "device_common.h"
 

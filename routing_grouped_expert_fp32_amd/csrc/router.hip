@@ -7,13 +7,17 @@
 // 的 Beam 并驱动其生产 API" §Dense Layers and Grouped MoE Routing (bias used to choose; FP32 routing
 // coefficients).
 //
-// router_logits: logits = x . W_r^T on the FP32 matrix cores (v_mfma_f32_16x16x4_f32). Accuracy:
-//   the 5120-long dot products are split into 8 partial chains per output (4 waves over K quarters,
-//   2 alternating accumulators per wave), summed in a fixed order, so the FP32 rounding error stays
-//   ~8x below a single serial chain. Output per (t, e): s = sigmoid(logit), b = s + bias[e].
-// router_partial (small batches): the same products split over 256-wide hidden chunks into more
-//   workgroups (a handful of tokens would leave W_r streamed by a few CUs); partial logits are
-//   summed in chunk order by the selection.
+// Three ways to the same logits (FP32 sums of exact products), chosen by batch size and dtype
+// (host_rules.cpp):
+// router_partial (up to 1024 tokens): logits = x . W_r^T on the FP32 matrix cores
+//   (v_mfma_f32_16x16x4_f32), split over 256-wide hidden chunks into many workgroups (a few tokens
+//   would leave W_r streamed by a few CUs); the selection sums the partial logits in chunk order.
+// router_split + router_fused (bf16 x past 1024 tokens): W_r split exactly into three bf16 planes
+//   once per call, then one workgroup per 32 tokens computes all 256 logits on the bf16 matrix
+//   cores, keeps them in LDS and selects there: nothing but the routes leaves the chip.
+// router_logits (FP32 x past 1024 tokens): FP32 matrix cores, 8 partial chains per output (4 waves
+//   over K quarters, 2 alternating accumulators per wave) summed in a fixed order; writes
+//   s = sigmoid(logit), b = s + bias[e] per (t, e) for router_select.
 // router_select: one wave per token, no sort (route_select.h).
 #include "device_common.h"
 #include "route_select.h"
@@ -26,8 +30,8 @@ namespace beam {
 // row (B); MFMA step c consumes component c, so step c sums K offsets {c, 4+c, 8+c, 12+c}: the same
 // permutation on both operands, hence the same products.
 // Tiles past 64 tokens: 64 tokens x 64 experts (each workgroup reads its 1.3 MB W_r slice for twice
-// as many tokens as with 32-token tiles: 0.275 -> 0.225 ms at T=8192, 1.03 -> 0.845 ms at
-// T=32768), two workgroups per CU by registers and LDS; 128-token tiles spill. Loading the next
+// as many tokens as with 32-token tiles: 0.275 -> 0.225 ms at T=8192 with bf16 x, 1.03 -> 0.845 ms
+// at T=32768), two workgroups per CU by registers and LDS; 128-token tiles spill. Loading the next
 // 16-deep step's operands ahead of the current MFMAs measured slower.
 template <bool XBF16, int TM, int EB>
 __global__ __launch_bounds__(256, TM >= 64 ? 2 : 4) void router_logits_kernel(
