@@ -232,21 +232,26 @@ struct ScoresFromLogits {
   }
 };
 
-// WG = 8 waves, 32 tokens x all E experts (E <= 256, E % 16 == 0). Wave w owns the expert tiles
-// w and w + 8 (16 experts each) for both 16-token tiles, over the whole hidden dimension, in 32-deep
-// MFMA steps. Token rows go through an LDS ring of 256-wide hidden chunks (rows padded to 528 B so
-// the 16 rows of a fragment read fall on distinct banks), loaded into registers one chunk ahead
-// and stored after the chunk's MFMAs; each wave's weight fragments (three planes) stream from L2
-// straight into registers, kPrefW steps ahead. Then the logits go to LDS and each wave selects 4
-// tokens (select_token).
-constexpr int kRfTM = 32, kRfWaves = 8, kRfChunk = 256, kRfRowBytes = 2 * kRfChunk + 16;
+// WG = 8 waves, kRfTM tokens (32; 64 past 8192 tokens) x all E experts (E <= 256, E % 16 == 0).
+// Wave w owns the expert tiles w and w + 8 (16 experts each) for every 16-token tile, over the
+// whole hidden dimension, in 32-deep MFMA steps. Token rows go through an LDS ring of 256-wide
+// hidden chunks (rows padded to 528 B so the 16 rows of a fragment read fall on distinct banks),
+// loaded into registers one chunk ahead and stored after the chunk's MFMAs; each wave's weight
+// fragments (three planes) stream from L2 straight into registers, kPrefW steps ahead. Then the
+// logits go to LDS and each wave selects kRfTM / 8 tokens (select_token).
+// Past 8192 tokens the workgroups take 64 tokens (half the weight stream per token; a workgroup's
+// time is set by its 7.5 MB weight stream either way), with two weight steps in flight.
+constexpr int kRfWaves = 8, kRfChunk = 256, kRfRowBytes = 2 * kRfChunk + 16;
 constexpr int kRfSteps = kRfChunk / 32;   // MFMA steps per chunk
-constexpr int kPrefW = 4;                 // weight steps in flight
+constexpr int64_t kRfWideT = 8192;        // batches past this use 64-token workgroups
+template <int kRfTM, int kPrefW>
 __global__ __launch_bounds__(64 * kRfWaves, 1) void router_fused_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
     const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wout, int64_t T,
     int H, int E, int G, int Gk, int K, float scale) {
   constexpr int MB = kRfTM / 16, NB = 2;
+  // token-row chunk: kRfTM rows x 32 16-byte pieces, TPR threads per row, PPT pieces each
+  constexpr int TPR = 64 * kRfWaves / kRfTM, PPT = 32 / TPR;
   __shared__ __attribute__((aligned(16))) unsigned char xs[2][kRfTM * kRfRowBytes];
   __shared__ float zl[kRfTM][256 + 1];
   __shared__ float bl[kRfWaves][256];
@@ -257,20 +262,20 @@ __global__ __launch_bounds__(64 * kRfWaves, 1) void router_fused_kernel(
   const int64_t t0 = (int64_t)blockIdx.x * kRfTM;
   const int n_et = E / 16;
 
-  // token-row chunk loads: thread -> row tid / 16, 16-byte pieces tid % 16 and tid % 16 + 16
-  const int xr = tid >> 4, xc = tid & 15;
+  // token-row chunk loads: thread -> row tid / TPR, 16-byte pieces tid % TPR + TPR i, i < PPT
+  const int xr = tid / TPR, xc = tid % TPR;
   const int64_t xrow = min(t0 + xr, T - 1);   // tail rows re-read a valid row
   const uint16_t* xsrc = x + xrow * H + 8 * xc;
-  u32x4 xv[2];
+  u32x4 xv[PPT];
   auto load_x = [&](int chunk) {
     const uint16_t* p = xsrc + chunk * kRfChunk;
-    xv[0] = *reinterpret_cast<const u32x4*>(p);
-    xv[1] = *reinterpret_cast<const u32x4*>(p + 128);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) xv[i] = *reinterpret_cast<const u32x4*>(p + 8 * TPR * i);
   };
   auto store_x = [&](int slot) {
     unsigned char* d = xs[slot] + xr * kRfRowBytes + 16 * xc;
-    *reinterpret_cast<u32x4*>(d) = xv[0];
-    *reinterpret_cast<u32x4*>(d + 256) = xv[1];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) *reinterpret_cast<u32x4*>(d + 16 * TPR * i) = xv[i];
   };
 
   // weight fragments of expert tile nt = wave + 8 i, in fragment order (router_split_kernel): lane
@@ -395,9 +400,15 @@ hipError_t launch_router_fused(const void* x, const uint16_t* planes, const floa
                                int32_t* ids, float* w, const Shape& s, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   if (!use_fused_router(s, true)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(router_fused_kernel, dim3((unsigned)ceil_div(s.T, kRfTM)),
-                     dim3(64 * kRfWaves), 0, st, reinterpret_cast<const uint16_t*>(x), planes,
-                     bias, ids, w, s.T, s.H, s.E, s.G, s.Gk, s.K, s.scale);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  if (s.T > kRfWideT)
+    hipLaunchKernelGGL((router_fused_kernel<64, 2>), dim3((unsigned)ceil_div(s.T, 64)),
+                       dim3(64 * kRfWaves), 0, st, xb, planes, bias, ids, w, s.T, s.H, s.E, s.G,
+                       s.Gk, s.K, s.scale);
+  else
+    hipLaunchKernelGGL((router_fused_kernel<32, 4>), dim3((unsigned)ceil_div(s.T, 32)),
+                       dim3(64 * kRfWaves), 0, st, xb, planes, bias, ids, w, s.T, s.H, s.E, s.G,
+                       s.Gk, s.K, s.scale);
   return hipGetLastError();
 }
 
