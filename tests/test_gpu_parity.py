@@ -169,10 +169,11 @@ def test_skew_bf16_sampled(beam_bf16):
     assert err <= parity.TOL["bf16"]
 
 
-# 16 / 17: last fused selection-and-align launch / first separate one; 64 / 65: last split-hidden
-# router and single-workgroup align / first 64-token router tiles (the second holding one token);
-# 128 / 129: last small-block and first tiled expert GEMMs
-@pytest.mark.parametrize("T", [1, 3, 16, 17, 64, 65, 77, 128, 129, 300])
+# 16 / 17: last fused selection-and-align launch / first separate one; 64 / 65: last single-workgroup
+# align / first three-kernel align; 128 / 129: last small-block and first tiled expert GEMMs;
+# 1024 / 1025: last partial-logit router / first one-pass router (a 1-token last workgroup);
+# 8193: first 64-token one-pass router workgroups (the last holding one token)
+@pytest.mark.parametrize("T", [1, 3, 16, 17, 64, 65, 77, 128, 129, 300, 1024, 1025, 8193])
 def test_ragged_token_counts(beam_bf16, T):
     wl, d = _inputs("decode", beam_bf16, T=T)
     _say("ragged decode-shape forward T =", T)
