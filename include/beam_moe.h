@@ -85,7 +85,8 @@ enum { BEAM_F32 = 0, BEAM_BF16 = 1, BEAM_FP8_E4M3 = 2 };
  *                point; BEAM_BF16 / BEAM_FP8_E4M3 experts require x_dtype BEAM_BF16.
  *   out_dtype    BEAM_F32 (graded output) or BEAM_BF16 (round-to-nearest-even copy)
  * Limits of this library version: H % 256 == 0, F % 256 == 0, E <= 256, E % 16 == 0 and (E <= 64 or
- * E % 64 == 0), K <= 16, G <= 64, H * F < 2^31, T * K < 2^31. */
+ * E % 64 == 0), K <= 16, G <= 64, H * F < 2^31, T * K < 2^31; calls that run the experts on
+ * BEAM_BF16 activations also need T * H < 2^31 (x under 4 GiB). */
 typedef struct beam_moe_cfg {
   int32_t hidden;
   int32_t n_experts;
@@ -199,7 +200,8 @@ BEAM_API beam_status_t beam_moe_forward_routed(const void* x, const int32_t* top
  *   w_gate_up_scale [2 d_ff], w_down_scale [hidden]: FP32 per-output-channel scales for FP8 weights
  *              (activations then quantised on the fly as in beam_moe_forward); NULL otherwise
  *   workspace  device scratch of at least beam_dense_mlp_workspace_bytes(hidden, d_ff, w_dtype, T)
- * Limits: hidden % 256 == 0, d_ff % 256 == 0, hidden * d_ff < 2^31. Errors as for beam_moe_forward. */
+ * Limits: hidden % 256 == 0, d_ff % 256 == 0, hidden * d_ff < 2^31, T * hidden < 2^31. Errors as
+ * for beam_moe_forward. */
 BEAM_API beam_status_t beam_dense_mlp_forward(const void* x, const void* w_gate_up,
                                               const void* w_down, void* out, int64_t T,
                                               int32_t hidden, int32_t d_ff, int32_t w_dtype,

@@ -136,9 +136,16 @@ beam_status_t check_cfg(const beam_moe_cfg* c, bool experts) {
   return BEAM_OK;
 }
 
-beam_status_t check_T(const beam_moe_cfg* c, int64_t T) {
+// bf16 activations under 4 GiB: the tiled expert GEMM gathers token rows with 32-bit offsets
+bool x_fits_offsets(int64_t T, int64_t hidden) {
+  return (uint64_t)T * (uint64_t)hidden < (uint64_t(1) << 31);
+}
+
+beam_status_t check_T(const beam_moe_cfg* c, int64_t T, bool experts) {
   if (T < 0) return BEAM_ERR_SHAPE;
   if (T * c->topk >= (int64_t(1) << 31) || T >= (int64_t(1) << 31)) return BEAM_ERR_UNSUPPORTED;
+  if (experts && c->x_dtype == BEAM_BF16 && !x_fits_offsets(T, c->hidden))
+    return BEAM_ERR_UNSUPPORTED;
   return BEAM_OK;
 }
 
@@ -397,7 +404,7 @@ beam_status_t check_dense(int32_t hidden, int32_t d_ff, int32_t w_dtype, int32_t
   if (w_dtype != BEAM_BF16 && w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
   if (out_dtype != BEAM_F32 && out_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
   if (hidden % 256 != 0 || d_ff % 256 != 0 || (int64_t)hidden * d_ff >= (int64_t(1) << 31) ||
-      T >= (int64_t(1) << 31))
+      T >= (int64_t(1) << 31) || !x_fits_offsets(T, hidden))
     return BEAM_ERR_UNSUPPORTED;
   return BEAM_OK;
 }
@@ -421,7 +428,7 @@ beam_status_t forward_impl(const void* x, const float* w_router, const float* bi
                            void* workspace, size_t workspace_bytes, void* stream) {
   beam_status_t rc = check_cfg(cfg, true);
   if (rc != BEAM_OK) return rc;
-  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T, true)) != BEAM_OK) return rc;
   const beam_moe_cfg& c = *cfg;
   const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
   if (!fp8 && (w_gate_up_scale || w_down_scale)) return BEAM_ERR_DTYPE;
@@ -528,7 +535,7 @@ beam_status_t beam_moe_workspace_region(const beam_moe_cfg* cfg, int64_t T, int3
                                         size_t* offset, size_t* bytes) {
   beam_status_t rc = check_cfg(cfg, true);
   if (rc != BEAM_OK) return rc;
-  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T, true)) != BEAM_OK) return rc;
   if (!offset || !bytes) return BEAM_ERR_NULL;
   return region_of(*cfg, make_layout(*cfg, T, true), T, 1, region, offset, bytes);
 }
@@ -560,7 +567,7 @@ beam_status_t beam_moe_route(const void* x, const float* w_router, const float* 
                              void* stream) {
   beam_status_t rc = check_cfg(cfg, false);
   if (rc != BEAM_OK) return rc;
-  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T, false)) != BEAM_OK) return rc;
   if (T == 0) return BEAM_OK;
   const beam_moe_cfg& c = *cfg;
   if (!x || !w_router || !bias || !topk_ids || !topk_w || !workspace) return BEAM_ERR_NULL;
@@ -608,7 +615,7 @@ beam_status_t beam_moe_forward_noalloc(const void* x, const float* w_router, con
                                        int32_t* topk_ids_out, float* topk_w_out, void* stream) {
   beam_status_t rc = check_cfg(cfg, true);
   if (rc != BEAM_OK) return rc;
-  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T, true)) != BEAM_OK) return rc;
   if (T == 0) return BEAM_OK;
   if (make_layout(*cfg, T, true).total > beam::kScratchBytes) return BEAM_ERR_WORKSPACE;
   if ((rc = check_device()) != BEAM_OK) return rc;
@@ -656,7 +663,7 @@ beam_status_t beam_moe_forward_boundary(const void* x, const float* w_router, co
                                         size_t workspace_bytes, void* stream) {
   beam_status_t rc = check_cfg(cfg, true);
   if (rc != BEAM_OK) return rc;
-  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T, true)) != BEAM_OK) return rc;
   const beam_moe_cfg& c = *cfg;
   if (c.x_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;   // the residual stream is bf16
   const bool fp8 = c.w_dtype == BEAM_FP8_E4M3;
@@ -725,7 +732,7 @@ beam_status_t beam_moe_forward_routed(const void* x, const int32_t* topk_ids, co
                                       size_t workspace_bytes, void* stream) {
   beam_status_t rc = check_cfg(cfg, true);
   if (rc != BEAM_OK) return rc;
-  if ((rc = check_T(cfg, T)) != BEAM_OK) return rc;
+  if ((rc = check_T(cfg, T, true)) != BEAM_OK) return rc;
   const beam_moe_cfg& c = *cfg;
   if (expert_begin < 0 || expert_begin > expert_end || expert_end > c.n_experts)
     return BEAM_ERR_SHAPE;

@@ -103,6 +103,9 @@ def test_unsupported_shapes():
     assert _fwd(_cfg(d_ff=2500)) == UNSUP
     assert _fwd(_cfg(n_experts=512, n_groups=8)) == UNSUP
     assert _fwd(_cfg(topk=17, topk_groups=8)) == UNSUP
+    big_T = (1 << 31) // 5120 + 1                          # bf16 x of 4 GiB or more
+    assert _fwd(_cfg(), T=big_T) == UNSUP
+    assert _fwd(_cfg(), T=big_T - 1, ws_bytes=0) == WS      # one token less passes the size check
 
 
 def test_zero_tokens_is_a_noop():
@@ -215,6 +218,7 @@ def test_dense_mlp_validation():
     assert _dense(H=5000) == UNSUP
     assert _dense(F=20000) == UNSUP
     assert _dense(H=65536, F=65536) == UNSUP                # hidden * d_ff >= 2^31
+    assert _dense(T=(1 << 31) // 5120 + 1) == UNSUP         # bf16 x of 4 GiB or more
     assert _dense(T=0, x=None, out=None, ws=None) == OK
     assert _dense(x=None) == NULL
     assert _dense(wdt=bm.BEAM_FP8_E4M3) == NULL             # fp8 needs both scale arrays
