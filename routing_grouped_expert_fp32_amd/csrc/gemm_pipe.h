@@ -70,28 +70,6 @@ struct PipeCfg {
 // 8 ways in the XCD's L2
 constexpr int kPGroup = 4;
 
-// cache-policy operand of the direct loads: non-temporal for the weight stream of a one-block
-// expert (its weight tile is read once, so it should not push the shared token rows out of L2)
-constexpr int kCachePolicyNT = 2;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// 16-byte load per lane from the raw buffer [base, base + bytes) straight into LDS: lane offset
-// voff, wave-uniform offset soff; lanes outside the range read zero. Buffer loads rather than
-// global ones because the compiler then waits for LDS reads by count (lgkmcnt(n)) instead of
-// draining them all before every MFMA group.
-template <int kAux>
-__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t bytes, uint32_t voff,
-                                                  uint32_t soff, lds_void_t* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      // descriptor word 3: 32-bit data format (untyped loads still need a valid one)
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000),
-      dst, 16, voff, soff, 0, kAux);
-}
-
-// s_waitcnt immediate (gfx9 encoding) waiting until at most n vector-memory ops are outstanding
-constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
-
 // Workgroup barrier without the memory fence __syncthreads() adds (that fence waits for every
 // outstanding load, which would drain the prefetch). The empty asm statements keep the compiler
 // from moving memory accesses across it; LDS written by direct loads is visible once the issuing

@@ -1,11 +1,13 @@
 // Weight-streaming grouped GEMM for small row blocks (<= 16 rows; decode-sized batches), gfx950.
 //
 // At decode each touched expert carries a handful of rows, so every weight byte is used once or
-// twice: the kernel is an HBM stream. WG = 4 waves x 16 output columns; each lane streams its
-// weight row(s) straight from HBM into MFMA operand registers (no LDS), 512 bytes of every row per
-// batch with all of a batch's loads issued before its MFMAs (a row's last bytes short of a batch go
-// one MFMA step at a time). Token rows past the block's rows are
-// zero operands and their results are discarded.
+// twice: the kernels are HBM streams. The K-split kernel (below) is the one decode shapes use;
+// the column-tiled kernel covers rows that do not split into whole batches: WG = 4 waves x 16
+// output columns, each lane streaming its weight row(s) straight from HBM into MFMA operand
+// registers, 512 bytes of every row per batch with all of a batch's loads issued before its MFMAs
+// (a row's last bytes short of a batch go one MFMA step at a time). Token rows past the block's
+// rows are zero operands (the K-split kernel re-reads row 0 instead); their results are
+// discarded.
 //   bf16: v_mfma_f32_16x16x32_bf16, lane = row (l % 16), 16 bytes at K slice 8*(l/16) of each
 //         32-deep step; 8 steps per batch.
 //   FP8:  16x16x128 f8f6f4 MFMA (E4M3, unit block scales), 32 bytes at K slice 32*(l/16) of each
@@ -136,13 +138,16 @@ __global__ __launch_bounds__(256) void grouped_small_kernel(
 // KSW) split K (many more workgroups than the column-tiled kernel, which matters when a handful
 // of tokens touch few experts): wave w takes batches w, w + KSW, w + 2 KSW, ... of every row, so
 // at any moment a workgroup reads one contiguous stretch of each row (0.5-1.5% faster than
-// contiguous per-wave parts). Each wave keeps two batches of loads in flight (the next batch is
-// issued before the current one's MFMAs); the partial tiles are summed in LDS in wave order
-// (deterministic) and wave 0 runs the epilogue. Requires the rows to split into KSW x whole
-// batches.
+// contiguous per-wave parts). Weight batches travel HBM -> LDS through non-temporal direct loads
+// of whole 128-byte lines (6.3 -> 6.9 TB/s on the decode gate/up stream against register loads,
+// which can fetch only half a line per row per instruction in MFMA operand order); each wave
+// owns two LDS slots and keeps the next batch in flight while it computes the current one, and
+// reads back only what it loaded itself, so no workgroup barrier is needed. The partial tiles
+// are summed in LDS in wave order (deterministic) and wave 0 runs the epilogue. Requires the
+// rows to split into KSW x whole batches.
 template <bool FP8>
 struct KsBatch {
-  static constexpr int kBytes = 256;   // bf16: 4 steps of 64 B; FP8: 2 steps of 128 B
+  static constexpr int kBytes = 256;   // bf16: 4 steps of 64 B
 };
 template <>
 struct KsBatch<true> {
@@ -159,67 +164,131 @@ __global__ __launch_bounds__(64 * KSW) void grouped_small_ks_kernel(
     void* __restrict__ out, AlignTables at, int Kd, int Nout,
     int topk, const float* __restrict__ a_scale, const float* __restrict__ w_scale) {
   using M = SmallMath<FP8>;
-  constexpr int U = KsBatch<FP8>::kBytes / M::kStepBytes;   // MFMA steps per batch
-  constexpr int NACC = 2;   // gate/up: a gate and an up row per lane; down: two 16-column groups
-  constexpr int kKsWaves = KSW;
-  __shared__ floatx4 red[kKsWaves][NACC][64];
+  constexpr int BB = KsBatch<FP8>::kBytes;
+  constexpr int U = BB / M::kStepBytes;   // MFMA steps per batch
+  constexpr int LINES = BB / 128;         // 128-byte lines of each weight row per batch
+  constexpr int NLD = 4 * LINES;          // direct loads per batch: 32 rows, 8 rows per load
+  constexpr int A_OPS = U * (M::kLaneBytes / 16);   // token-row loads per batch
+  constexpr int kSlot = NLD * 1024;
+  constexpr int kRing = KSW * 2 * kSlot;  // two batch slots per wave
+  // one LDS array: the weight rings, then the K-split partial tiles
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kRing + KSW * 2 * 64 * 16];
+  floatx4(*red)[2][64] = reinterpret_cast<floatx4(*)[2][64]>(smem + kRing);
   const int b = blockIdx.y;
   if (b >= at.n_blocks[0]) return;
   const int e = at.blk_expert[b], row0 = at.blk_row0[b], rows = at.blk_rows[b];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int c0 = blockIdx.x * (GATE_UP ? 16 : 32);
   const int64_t row_bytes = (int64_t)Kd * M::kElemBytes;
-  constexpr int64_t BB = KsBatch<FP8>::kBytes;
-  const int64_t kq = row_bytes / kKsWaves, kbeg = wave * BB;   // batches wave, wave + KSW, ...
+  const int nb = (int)(row_bytes / KSW / BB);   // batches of this wave: wave, wave + KSW, ...
+  constexpr uint32_t SB = (uint32_t)BB * KSW;   // bytes between a wave's batches
+  const uint32_t kbeg = (uint32_t)wave * BB;
 
-  const unsigned char* ap = nullptr;
-  if (r < rows) {
-    if constexpr (GATE_UP)
-      ap = A + (int64_t)(at.sorted_slot[row0 + r] / topk) * row_bytes + kbeg;
-    else
-      ap = A + (int64_t)(row0 + r) * row_bytes + kbeg;
+  // token rows into registers through a buffer (x, under 4 GiB, or the block's rows of h);
+  // padding rows re-read row 0 (their results are discarded)
+  const int rr = r < rows ? r : 0;
+  const unsigned char* abase = GATE_UP ? A : A + (int64_t)row0 * row_bytes;
+  const uint32_t abytes = GATE_UP ? 0xffffffffu : (uint32_t)(rows * row_bytes);
+  const uint32_t aoff =
+      (uint32_t)((GATE_UP ? (int64_t)(at.sorted_slot[row0 + rr] / topk) : (int64_t)rr) *
+                 row_bytes) + kbeg + g * M::kLaneBytes;
+
+  // weight rows of the workgroup, 0..31: gate/up 16 gate rows then the 16 matching up rows; down
+  // 32 output columns. They arrive through non-temporal direct loads of whole 128-byte lines (a
+  // line fetched by halves into registers is fetched twice once it bypasses L2 retention):
+  // load (group rg of 8 rows, line ln) lands 1 KB in LDS, lane -> row 8 rg + lane / 8, LDS chunk
+  // lane % 8 holding line chunk (lane % 8) ^ (row % 8), so a fragment read of 16 rows is
+  // conflict-free. Buffers: the expert's gate half and up half (down: its matrix).
+  const unsigned char* wb0 = W + (int64_t)e * (GATE_UP ? 2 : 1) * Nout * row_bytes;
+  const unsigned char* wb1 = GATE_UP ? wb0 + (int64_t)Nout * row_bytes : wb0;
+  const uint32_t wbytes = (uint32_t)(Nout * row_bytes);
+  const int lrow = lane >> 3, gch = (lane & 7) ^ lrow;
+  uint32_t voff[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    const int wr = 8 * rg + lrow;
+    voff[rg] = (uint32_t)((c0 + (GATE_UP ? (wr & 15) : wr)) * row_bytes) + kbeg + gch * 16;
   }
-  const unsigned char* bp0;
-  const unsigned char* bp1 = nullptr;
-  if constexpr (GATE_UP) {
-    bp0 = W + ((int64_t)e * 2 * Nout + c0 + r) * row_bytes + kbeg;
-    bp1 = W + ((int64_t)e * 2 * Nout + Nout + c0 + r) * row_bytes + kbeg;
-  } else {
-    bp0 = W + ((int64_t)e * Nout + c0 + r) * row_bytes + kbeg;
-    bp1 = bp0 + 16 * row_bytes;
-  }
-  const int koff = g * M::kLaneBytes;
+  unsigned char* const ring = smem + wave * 2 * kSlot;
+  // LDS byte offset of this lane's 16-byte piece `piece` (0..7 within a line) of weight row wr
+  auto frag_at = [&](int wr, int ln, int piece) {
+    return ((wr >> 3) * LINES + ln) * 1024 + (wr & 7) * 128 + ((piece ^ (wr & 7)) << 4);
+  };
+
   floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  typename M::frag a[2][U], w0[2][U], w1[2][U];
-  auto load = [&](int buf, int64_t k) {
+  typename M::frag a[2][U];
+  // batch i of this wave into slot buf. live == false issues the same loads against empty
+  // buffers (no memory access, zeros): every trip then issues the same number of loads, so the
+  // wait counts below are exact on every path.
+  auto issue = [&](int buf, int i, bool live) {
+    const uint32_t kb = (uint32_t)i * SB;
+    const uint32_t ab = __builtin_amdgcn_readfirstlane(live ? abytes : 0u);
+    const uint32_t wbb = __builtin_amdgcn_readfirstlane(live ? wbytes : 0u);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      w0[buf][u] = M::load(bp0 + k + u * M::kStepBytes + koff);
-      w1[buf][u] = M::load(bp1 + k + u * M::kStepBytes + koff);
+      if constexpr (FP8) {
+        const u32x4 lo = buffer_load16<0>(abase, ab, aoff, kb + u * M::kStepBytes);
+        const u32x4 hi = buffer_load16<0>(abase, ab, aoff + 16, kb + u * M::kStepBytes);
+        a[buf][u] = typename M::frag{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      } else {
+        a[buf][u] = __builtin_bit_cast(bf16x8, buffer_load16<0>(abase, ab, aoff,
+                                                                kb + u * M::kStepBytes));
+      }
     }
+    unsigned char* slot = ring + buf * kSlot;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      a[buf][u] = ap ? M::load(ap + k + u * M::kStepBytes + koff) : M::zero();
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int ln = 0; ln < LINES; ++ln)
+        buffer_load_lds16<kCachePolicyNT>(rg < 2 ? wb0 : wb1, wbb, voff[rg] + ln * 128, kb,
+                                          (lds_void_t*)(slot + (rg * LINES + ln) * 1024));
   };
-  auto mma = [&](int buf) {
+  auto compute = [&](int buf) {
+    const unsigned char* slot = ring + buf * kSlot;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      acc0 = M::mma(a[buf][u], w0[buf][u], acc0);
-      acc1 = M::mma(a[buf][u], w1[buf][u], acc1);
+      const int ln = (u * M::kStepBytes) / 128, p0 = (u * M::kStepBytes) % 128 / 16;
+      typename M::frag w0, w1;
+      if constexpr (FP8) {
+        const intx4 l0 = *reinterpret_cast<const intx4*>(slot + frag_at(r, ln, p0 + 2 * g));
+        const intx4 h0 = *reinterpret_cast<const intx4*>(slot + frag_at(r, ln, p0 + 2 * g + 1));
+        const intx4 l1 = *reinterpret_cast<const intx4*>(slot + frag_at(16 + r, ln, p0 + 2 * g));
+        const intx4 h1 =
+            *reinterpret_cast<const intx4*>(slot + frag_at(16 + r, ln, p0 + 2 * g + 1));
+        w0 = typename M::frag{l0.x, l0.y, l0.z, l0.w, h0.x, h0.y, h0.z, h0.w};
+        w1 = typename M::frag{l1.x, l1.y, l1.z, l1.w, h1.x, h1.y, h1.z, h1.w};
+      } else {
+        w0 = *reinterpret_cast<const bf16x8*>(slot + frag_at(r, ln, p0 + g));
+        w1 = *reinterpret_cast<const bf16x8*>(slot + frag_at(16 + r, ln, p0 + g));
+      }
+      acc0 = M::mma(a[buf][u], w0, acc0);
+      acc1 = M::mma(a[buf][u], w1, acc1);
     }
   };
-  const int nb = (int)(kq / BB);
-  constexpr int64_t SB = BB * KSW;   // bytes between a wave's batches
-  load(0, 0);
+  // Each wave reads only what it loaded itself: no barrier, its own vmcnt wait makes a slot
+  // visible; a slot is refilled only after the reads of its previous batch have returned.
+  constexpr int kBatchOps = A_OPS + NLD;
+  issue(0, 0, true);
   int i = 0;
-  for (; i + 2 <= nb; i += 2) {   // two batches per trip so the buffers stay in registers
-    load(1, (int64_t)(i + 1) * SB);
-    mma(0);
-    if (i + 2 < nb) load(0, (int64_t)(i + 2) * SB);
-    mma(1);
+  for (; i + 2 <= nb; i += 2) {   // two batches per trip so the token fragments stay in registers
+    issue(1, i + 1, true);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBatchOps));   // batch i has landed
+    compute(0);
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);   // slot 0's reads are done before it is refilled
+    __builtin_amdgcn_sched_barrier(0);
+    issue(0, i + 2, i + 2 < nb);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBatchOps));   // batch i + 1 has landed
+    compute(1);
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (i < nb) mma(0);   // odd count: batch nb-1 was loaded into buffer 0
+  if (i < nb) {   // odd count: batch nb-1 was issued into slot 0
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compute(0);
+  }
 
   red[wave][0][lane] = acc0;
   red[wave][1][lane] = acc1;
@@ -227,7 +296,7 @@ __global__ __launch_bounds__(64 * KSW) void grouped_small_ks_kernel(
   if (wave != 0) return;
   floatx4 s0 = red[0][0][lane], s1 = red[0][1][lane];
 #pragma unroll
-  for (int w = 1; w < kKsWaves; ++w) {
+  for (int w = 1; w < KSW; ++w) {
     s0 += red[w][0][lane];
     s1 += red[w][1][lane];
   }
