@@ -366,8 +366,8 @@ def roofline(r, workload):
         roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": pk, "unit": "TFLOP/s",
                 "frac": g["TFLOPs"] / pk}
     fp8 = str(r["dtype"] == "fp8").lower()
-    if r["small_blocks"]:   # K split over 8 waves (bf16) or 4 (FP8) at the Beam shape
-        roof["kernel"] = f"gate_up: grouped_small_ks_kernel<true, {fp8}, {4 if fp8 == 'true' else 8}>"
+    if r["small_blocks"]:   # K split over 4 waves
+        roof["kernel"] = f"gate_up: grouped_small_ks_kernel<true, {fp8}, 4>"
     else:
         roof["kernel"] = f"gate_up: grouped_pipe_kernel<true, {fp8}>"
     roof["algorithmic_bytes_per_launch"] = g["bytes"]

@@ -41,13 +41,6 @@ static void launch_one(const void* a, const void* w, void* out,
     const int64_t row_bytes = (int64_t)Kd * (FP8 ? 1 : 2);
     constexpr int64_t BB = KsBatch<FP8>::kBytes;
     const dim3 grid(Nout / (GATE_UP ? 16 : 32), (unsigned)max_blocks);
-    if constexpr (GATE_UP && !FP8) {
-      if ((row_bytes / 8) % BB == 0) {
-        hipLaunchKernelGGL((grouped_small_ks_kernel<GATE_UP, FP8, 8>), grid, dim3(512), 0, st, A,
-                           W, out, at, Kd, Nout, topk, a_scale, w_scale);
-        return;
-      }
-    }
     if ((row_bytes / 4) % BB == 0) {
       hipLaunchKernelGGL((grouped_small_ks_kernel<GATE_UP, FP8, 4>), grid, dim3(256), 0, st, A, W,
                          out, at, Kd, Nout, topk, a_scale, w_scale);

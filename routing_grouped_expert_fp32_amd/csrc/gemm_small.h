@@ -154,10 +154,9 @@ struct KsBatch<true> {
   static constexpr int kBytes = 128;   // one 128-deep FP8 step (the quarter of 2560 is 640 B)
 };
 
-// KSW = waves splitting K: 8 for bf16 gate/up where its rows split into whole batches
-// (shorter-lived workgroups, so less of the grid's tail runs part-empty: 0.996 -> 0.986 ms at
-// T=32), else 4 (FP8 gate/up measured 6% slower with 8: its eighths of a row are 5 one-step
-// batches).
+// KSW = waves splitting K, 4 for every launch: with the LDS slots, 8-wave bf16 gate/up workgroups
+// (144 KB of LDS, one per CU) measured 0.897 ms at T=32 against 0.875 ms for two 4-wave ones per
+// CU (whose starts and ends overlap); FP8 gate/up was 6% slower with 8 already with register loads.
 template <bool GATE_UP, bool FP8, int KSW>
 __global__ __launch_bounds__(64 * KSW) void grouped_small_ks_kernel(
     const unsigned char* __restrict__ A, const unsigned char* __restrict__ W,
