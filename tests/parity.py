@@ -23,8 +23,9 @@ _OUT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 
 
 def say(*a):
-    """Progress line of a long check: printed, and appended to gpurun_out/test_progress.log when
-    that folder exists (a captured test's progress is then still visible while it runs)."""
+    """Progress line of a long check: printed, and appended to test_progress.log in the run-output
+    folder at the repository root when that folder exists (a captured test's progress is then
+    still visible while it runs)."""
     msg = " ".join(str(x) for x in a)
     print(msg, flush=True)
     if os.path.isdir(_OUT):
