@@ -34,9 +34,9 @@ static void launch_one(const void* a, const void* w, void* out,
   const auto* A = reinterpret_cast<const unsigned char*>(a);
   const auto* W = reinterpret_cast<const unsigned char*>(w);
   if (small) {
-    // K split across the waves of 16-column (down: 32-column) workgroups: 4x or 8x the workgroups
-    // of the column-tiled grid (which leaves most CUs idle at a handful of tokens) and two batches
-    // in flight per wave; faster at every decode size measured (T = 1 .. 64). The column-tiled
+    // K split across the 4 waves of 16-column (down: 32-column) workgroups: 4x the workgroups of
+    // the column-tiled grid (which leaves most CUs idle at a handful of tokens) and two batches in
+    // flight per wave; faster at every decode size measured (T = 1 .. 64). The column-tiled
     // kernel covers the shapes whose rows do not split into whole batches.
     const int64_t row_bytes = (int64_t)Kd * (FP8 ? 1 : 2);
     constexpr int64_t BB = KsBatch<FP8>::kBytes;
