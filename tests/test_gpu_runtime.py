@@ -12,8 +12,8 @@ import synthgen
 
 pytestmark = pytest.mark.gpu
 
-# H 512, 32 experts in 8 groups (keep 2), top-4, d_ff 768: T=8 takes the small-block kernels,
-# T=700 (~87 rows per expert) the tiled ones
+# H 512, 32 experts in 8 groups (keep 2), top-4, d_ff 768: T=8 and T=32 take the small-block
+# kernels, T=700 (~87 rows per expert) the tiled ones
 SHAPE = synthgen.BeamShape(hidden=512, n_experts=32, n_groups=8, topk_groups=2, topk=4, d_ff=768)
 
 
@@ -37,7 +37,7 @@ def _case(w_dtype, T):
 
 
 @pytest.mark.parametrize("w_dtype,T",
-                         [("bf16", 8), ("bf16", 700), ("fp8", 700), ("bf16", 1100)])
+                         [("bf16", 8), ("fp8", 32), ("bf16", 700), ("fp8", 700), ("bf16", 1100)])
 def test_graph_replay_equals_eager(w_dtype, T):
     print("graph capture", w_dtype, "T =", T, flush=True)
     run, out, ids = _case(w_dtype, T)
